@@ -1,0 +1,111 @@
+"""Dynamic bf16 -> E4M3 KV quantization -- oracle side (test infrastructure only).
+
+Follows the HF blog "Blazingly fast whisper transcriptions with Inference
+Endpoints", section "Inference Stack" (activations are quantized dynamically
+and the KV cache stores one byte per element while compute stays bf16), and
+whisper-blaze 0.1.8 (PyPI page): the feature list ("FP8 quantize/dequantize
+with per-tensor scaling") and "Direct Kernel API" (``quantise_e4m3`` returns
+the codes and a scale; ``dequantise_e4m3`` takes the codes and that scale).
+
+Readings where the pages are silent:
+
+* the scale is the dequantization multiplier, ``x ~= decode(code) * scale``,
+  chosen so the group's largest magnitude maps to E4M3's largest finite value:
+  ``scale = float32(amax / 448)``; a group whose amax is 0 gets scale 1;
+* a scale group is the whole tensor (one scale) or one head (one scale per
+  head, over every sequence and valid position of the call); padding
+  positions (t >= lens[b]) never enter the abs-max;
+* the code is ``E4M3_RNE_saturating(float32(x / scale))``: the IEEE fp32
+  quotient (correctly rounded) followed by the E4M3 rounding -- two
+  roundings, in that order.
+
+Layouts: activations are logical ``[B][T][H][D]``; the cache is
+``[B][H][L][D]`` and sequence b's position t lands in slot ``dst_start[b] + t``.
+"""
+import numpy as np
+
+from . import e4m3
+
+PER_TENSOR = 0
+PER_HEAD = 1
+
+
+def valid_mask(B, T, lens):
+    """[B][T] boolean: position t of sequence b is valid when t < lens[b]."""
+    lens = np.asarray(lens, dtype=np.int64)
+    return np.arange(T)[None, :] < lens[:, None]
+
+
+def group_amax(x, lens, gran):
+    """Abs-max per scale group as float32: shape [1] (per tensor) or [H] (per head).
+
+    x: float32 array [B][T][H][D] holding bf16 values exactly.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    B, T, H, D = x.shape
+    mask = valid_mask(B, T, lens)
+    a = np.abs(x[mask])                        # [n_valid][H][D]
+    if gran == PER_TENSOR:
+        return np.array([a.max() if a.size else 0.0], dtype=np.float32)
+    if a.shape[0] == 0:
+        return np.zeros(H, dtype=np.float32)
+    return a.max(axis=(0, 2)).astype(np.float32)
+
+
+def scales_from_amax(amax):
+    """scale = float32(amax / 448), or 1 where amax is 0."""
+    amax = np.asarray(amax, dtype=np.float32)
+    s = amax / np.float32(e4m3.E4M3_MAX)      # IEEE fp32 division
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize(x, scale, gran):
+    """float32 [B][T][H][D] -> uint8 codes of the same shape."""
+    x = np.asarray(x, dtype=np.float32)
+    scale = np.asarray(scale, dtype=np.float32)
+    if gran == PER_TENSOR:
+        s = scale.reshape(1, 1, 1, 1)
+    else:
+        s = scale.reshape(1, 1, -1, 1)
+    with np.errstate(over="ignore"):           # an overflow to inf saturates below
+        y = (x / s).astype(np.float32)        # IEEE fp32 division per element
+    return e4m3.encode(y)
+
+
+def fill_cache(x, lens, dst_start, cache, scale, gran):
+    """Write codes of the valid positions into ``cache`` [B][H][L][D] (in place).
+
+    Slot ``dst_start[b] + t`` of sequence b receives position t < lens[b];
+    every other slot keeps its old byte.
+    """
+    B, T, H, D = x.shape
+    codes = quantize(x, scale, gran)           # [B][T][H][D]
+    for b in range(B):
+        n = int(lens[b])
+        s0 = int(dst_start[b])
+        cache[b, :, s0:s0 + n, :] = codes[b, :n].transpose(1, 0, 2)
+    return cache
+
+
+def quantize_kv(x, lens, dst_start, cache, gran):
+    """The whole dynamic step: scales from the valid abs-max, then the cache fill.
+
+    Returns the float32 scales ([1] or [H]); ``cache`` is written in place.
+    """
+    scale = scales_from_amax(group_amax(x, lens, gran))
+    fill_cache(x, lens, dst_start, cache, scale, gran)
+    return scale
+
+
+def dequantize(codes, scale, gran, head_axis):
+    """codes (uint8) -> float64 values ``decode(code) * scale`` (exact in fp64).
+
+    ``head_axis`` names the axis that indexes heads when ``gran`` is per head.
+    """
+    v = e4m3.decode(codes)
+    scale = np.asarray(scale, dtype=np.float64)
+    if gran == PER_TENSOR:
+        return v * scale.reshape(())
+    shape = [1] * v.ndim
+    shape[head_axis] = -1
+    return v * scale.reshape(shape)
