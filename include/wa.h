@@ -1,0 +1,171 @@
+/*
+ * wa.h -- C ABI of the Whisper attention hot path on MI355X (gfx950).
+ *
+ * Three operations, all asynchronous on the caller's HIP stream:
+ *
+ *   wa_kv_quant_fp8  bf16 -> float8 E4M3 quantization that fills a KV cache
+ *   wa_encoder_attn  dense bf16 softmax attention (encoder self-attention,
+ *                    or causal decoder prompt prefill), ragged by length
+ *   wa_decode_attn   one query token per sequence against an E4M3 KV cache
+ *                    (decoder self-attention or cross-attention)
+ *
+ * Sources for what is computed:
+ *   - "Blazingly fast whisper transcriptions with Inference Endpoints" (HF
+ *     blog), section "Inference Stack": activations are quantized on the fly
+ *     and the KV cache is stored as one-byte float8 while computation stays
+ *     in bfloat16.
+ *   - whisper-blaze 0.1.8 (PyPI page): feature list ("FP8 quantize/dequantize
+ *     with per-tensor scaling"; Flash Attention for encoder self-attention
+ *     and decoder self/cross-attention) and "Direct Kernel API"
+ *     (quantise_e4m3 returns codes and a scale; dequantise_e4m3 takes both;
+ *     encoder_self_attn and decoder_cross_attn take no mask, decoder_self_attn
+ *     a causal one).
+ *   - "Unlocking the power of OpenAI's Whisper", section 3 (encoder
+ *     self-attention over the audio frames; decoder self-attention over
+ *     previous tokens and cross-attention over the encoded audio).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked "device" point to GPU memory, owned by the caller; the
+ *     library allocates nothing and keeps no pointer after a call returns.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  head_dim must be 64
+ *     (WA_ERR_UNSUPPORTED otherwise); the head_dim axis has stride 1.
+ *     Other strides are in elements.  bf16 pointers must be 16-byte aligned
+ *     and their b/t/h strides multiples of 8; uint8 cache pointers and
+ *     workspaces 16-byte aligned, cache strides multiples of 16
+ *     (WA_ERR_UNSUPPORTED otherwise).
+ *   - Argument checks run on the host before any HIP call and launch nothing
+ *     on failure.  The first call on a device checks that it is a gfx950
+ *     (WA_ERR_UNSUPPORTED otherwise).  A failed launch returns WA_ERR_HIP.
+ *   - Length arrays live on the device, so a decode loop never waits on the
+ *     host.  Kernels clamp each length to [0, maximum]; positions at or
+ *     beyond a sequence's length are neither read nor written.
+ *   - No call synchronises; results are ready when the stream reaches them.
+ *     Calls keep no state and may be made from several host threads; two
+ *     calls in flight at once must not share a workspace.
+ */
+#ifndef WA_H
+#define WA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WA_OK = 0,
+  WA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum */
+  WA_ERR_UNSUPPORTED = 2,        /* head_dim != 64, misalignment, not gfx950 */
+  WA_ERR_WORKSPACE_TOO_SMALL = 3,
+  WA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} wa_status;
+
+typedef enum {
+  WA_SCALE_PER_TENSOR = 0,       /* one scale for the whole tensor: scale[1] */
+  WA_SCALE_PER_HEAD = 1          /* one scale per head: scale[H] */
+} wa_scale_gran;
+
+/* Element strides of the batch, position and head axes. */
+typedef struct {
+  int64_t b, t, h;
+} wa_strides;
+
+/*
+ * wa_kv_quant_fp8 -- quantize bf16 keys or values into an E4M3 KV cache.
+ *
+ * What: for every scale group g (the whole tensor, or head h) the
+ *   dequantization multiplier is scale[g] = fp32(amax_g / 448), where amax_g
+ *   is the largest |x| over the valid positions (t < lens[b]) of that group,
+ *   and scale[g] = 1 when amax_g is 0.  Each valid element becomes
+ *     code = E4M3(clamp(fp32(x / scale[g]), -448, 448))
+ *   with the IEEE fp32 quotient rounded to nearest even, then rounded to
+ *   nearest-even OCP E4M3 (max 448, sign kept, so -0 gives 0x80).  So
+ *   x ~= decode(code) * scale[g].  The pages name dynamic per-tensor E4M3
+ *   scaling (whisper-blaze "Direct Kernel API"; HF blog "Inference Stack");
+ *   the scale formula, rounding and per-head groups are the plain reading.
+ *
+ * x          device, bf16 [B][T_max][H][64] with strides xs.
+ * lens       device int32 [B], valid positions per sequence; NULL = T_max.
+ * dst_start  device int32 [B]; position t of sequence b goes to cache slot
+ *            dst_start[b] + t.  NULL = 0.  Slots outside [0, cache_len) are
+ *            skipped; untouched slots keep their bytes.
+ * cache      device uint8 [B][H][cache_len][64] with strides cs (t = slot).
+ * scale      device float32 [1] or [H] (gran).  compute_scale = 1: written
+ *            with the dynamic scales above.  compute_scale = 0: read as given
+ *            (a static scale, e.g. appending a decode token to a cache filled
+ *            earlier); values beyond 448 * scale saturate.
+ * workspace  device scratch of at least wa_kv_quant_fp8_workspace_size()
+ *            bytes (only used when compute_scale = 1; may be NULL otherwise).
+ *            Its contents need no initialisation.
+ */
+wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                          int head_dim, const int32_t *lens, const int32_t *dst_start,
+                          uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                          wa_scale_gran gran, int compute_scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gran);
+
+/*
+ * wa_encoder_attn -- dense softmax attention over bf16 Q/K/V.
+ *
+ * What: per sequence b, head h and query i < lens[b]:
+ *     O[i] = sum_j softmax_j(softmax_scale * Q[i] . K[j]) V[j]
+ *   over keys j < lens[b] (causal = 0: encoder self-attention, "no causal
+ *   mask" in whisper-blaze "Direct Kernel API") or j <= i (causal = 1:
+ *   decoder prompt prefill, the "causal mask" of decoder_self_attn).
+ *   Accumulation is fp32; O is written as bf16 (round to nearest even).
+ *   Rows i >= lens[b] of O are not written.
+ *
+ * q, k, v    device bf16 [B][T_max][H][64] with strides qs, ks, vs.
+ * o          device bf16 [B][T_max][H][64] with strides os; must not alias
+ *            q, k or v.
+ * lens       device int32 [B]; NULL = T_max for every sequence.
+ * softmax_scale  the score multiplier, e.g. 1/sqrt(64) = 0.125.
+ */
+wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+                          const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
+                          int H, int T_max, int head_dim, const int32_t *lens, int causal,
+                          float softmax_scale, hipStream_t stream);
+
+/*
+ * wa_decode_attn -- one query token per sequence against an E4M3 KV cache.
+ *
+ * What: per sequence b and head h, with n = lens[b] cached slots,
+ *     K^_j = decode(Kc[b,h,j]) * k_scale[g],  V^_j likewise (g = 0 or h),
+ *     o = sum_{j<n} softmax_j(softmax_scale * q . K^_j) V^_j
+ *   computed in fp32 from the bf16 query, written as bf16.  The query sits at
+ *   the last cached position, so the causal decoder self-attention of
+ *   whisper-blaze's decoder_self_attn sees every slot j < n (its own K/V
+ *   already appended at slot n - 1); cross-attention (decoder_cross_attn, no
+ *   mask) passes n = 1500 for every sequence.  n = 0 gives a zero row.  The
+ *   keys are split into chunks evaluated in parallel and merged with the
+ *   softmax rescaling identity.
+ *
+ * q          device bf16 [B][H][64]; qs.b and qs.h used (qs.t ignored).
+ * k_cache, v_cache  device uint8 [B][H][cache_len][64], both with strides cs.
+ * k_scale, v_scale  device float32 [1] or [H] (gran).
+ * lens       device int32 [B] (required).
+ * o          device bf16 [B][H][64]; os.b and os.h used.
+ * workspace  device scratch of at least wa_decode_attn_workspace_size() bytes;
+ *            needs no initialisation.
+ */
+wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                         const uint8_t *v_cache, wa_strides cs, int cache_len,
+                         const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                         const int32_t *lens, int B, int H, int head_dim, float softmax_scale,
+                         uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+size_t wa_decode_attn_workspace_size(int B, int H, int cache_len);
+
+/* Static, NUL-terminated description of a status code. */
+const char *wa_status_string(wa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WA_H */

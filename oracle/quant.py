@@ -75,15 +75,17 @@ def quantize(x, scale, gran):
 def fill_cache(x, lens, dst_start, cache, scale, gran):
     """Write codes of the valid positions into ``cache`` [B][H][L][D] (in place).
 
-    Slot ``dst_start[b] + t`` of sequence b receives position t < lens[b];
-    every other slot keeps its old byte.
+    Slot ``dst_start[b] + t`` of sequence b receives position t < lens[b]
+    when that slot lies in [0, L); every other slot keeps its old byte.
     """
     B, T, H, D = x.shape
+    L = cache.shape[2]
     codes = quantize(x, scale, gran)           # [B][T][H][D]
     for b in range(B):
-        n = int(lens[b])
-        s0 = int(dst_start[b])
-        cache[b, :, s0:s0 + n, :] = codes[b, :n].transpose(1, 0, 2)
+        for t in range(int(lens[b])):
+            slot = int(dst_start[b]) + t
+            if 0 <= slot < L:
+                cache[b, :, slot, :] = codes[b, t]
     return cache
 
 

@@ -1,0 +1,140 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol that
+include/wa.h declares, and rejects bad arguments on the host before any HIP
+call (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wa.h")
+
+
+@pytest.fixture(scope="module")
+def wa():
+    import whisper_attention_amd as wa
+    return wa
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wa_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_three_operations():
+    names = _declared()
+    for n in ("wa_kv_quant_fp8", "wa_encoder_attn", "wa_decode_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(wa):
+    for name in _declared():
+        assert hasattr(wa.lib, name), name
+    assert set(wa.EXPORTED) == set(_declared())
+
+
+def test_status_strings(wa):
+    for s in range(5):
+        assert wa.wa_status_string(s).startswith("WA_")
+    assert "unknown" in wa.wa_status_string(99)
+
+
+def test_workspace_sizes(wa):
+    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, 224, "head") > 0
+    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, 224, "tensor") > 0
+    assert wa.wa_kv_quant_fp8_workspace_size(0, 20, 224, "head") == 0
+    assert wa.wa_decode_attn_workspace_size(1, 6, 1500) > 0      # split keys -> partials
+    assert wa.wa_decode_attn_workspace_size(0, 6, 1500) == 0
+    # a big batch needs no split, hence no workspace
+    assert wa.wa_decode_attn_workspace_size(256, 20, 1500) == 0
+
+
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation
+MIS = 0x10002           # misaligned
+
+
+def _S(wa, b=20 * 64 * 1500, t=20 * 64, h=64):
+    return wa.Strides(b, t, h)
+
+
+def _quant(wa, **kw):
+    a = dict(x=FAKE, xs=_S(wa), B=2, H=20, T=1500, D=64, lens=None, dst=None, cache=FAKE,
+             cs=wa.Strides(20 * 1500 * 64, 64, 1500 * 64), L=1500, scale=FAKE, gran=0, cs_=1,
+             ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return wa.lib.wa_kv_quant_fp8(a["x"], a["xs"], a["B"], a["H"], a["T"], a["D"], a["lens"], a["dst"],
+                                  a["cache"], a["cs"], a["L"], a["scale"], a["gran"], a["cs_"],
+                                  a["ws"], a["wsb"], a["stream"])
+
+
+def test_quant_validation(wa):
+    assert _quant(wa, x=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, cache=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, scale=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, B=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, H=-1) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, L=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, gran=2) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, cs_=3) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, D=128) == wa.WA_ERR_UNSUPPORTED
+    assert _quant(wa, x=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _quant(wa, xs=_S(wa, t=20 * 64 + 4)) == wa.WA_ERR_UNSUPPORTED
+    assert _quant(wa, cs=wa.Strides(20 * 1500 * 64, 8, 1500 * 64)) == wa.WA_ERR_UNSUPPORTED
+    assert _quant(wa, ws=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant(wa, ws=MIS, wsb=1 << 20) == wa.WA_ERR_UNSUPPORTED
+    assert _quant(wa, wsb=16) == wa.WA_ERR_WORKSPACE_TOO_SMALL
+
+
+def _enc(wa, **kw):
+    s = _S(wa)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, qs=s, ks=s, vs=s, os=s, B=2, H=20, T=1500, D=64,
+             lens=None, causal=0, sc=0.125)
+    a.update(kw)
+    return wa.lib.wa_encoder_attn(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"],
+                                  a["B"], a["H"], a["T"], a["D"], a["lens"], a["causal"], a["sc"], None)
+
+
+def test_encoder_validation(wa):
+    for name in ("q", "k", "v", "o"):
+        assert _enc(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc(wa, T=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc(wa, causal=2) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc(wa, sc=0.0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc(wa, sc=float("nan")) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc(wa, D=80) == wa.WA_ERR_UNSUPPORTED
+    assert _enc(wa, o=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _enc(wa, ks=_S(wa, h=65)) == wa.WA_ERR_UNSUPPORTED
+
+
+def _dec(wa, **kw):
+    cs = wa.Strides(20 * 1500 * 64, 64, 1500 * 64)
+    a = dict(q=FAKE, qs=wa.Strides(20 * 64, 0, 64), kc=FAKE, vc=FAKE, cs=cs, L=1500, ks=FAKE, vs=FAKE,
+             gran=0, lens=FAKE, B=1, H=6, D=64, sc=0.125, o=FAKE, os=wa.Strides(20 * 64, 0, 64),
+             ws=FAKE, wsb=0)
+    a.update(kw)
+    return wa.lib.wa_decode_attn(a["q"], a["qs"], a["kc"], a["vc"], a["cs"], a["L"], a["ks"], a["vs"],
+                                 a["gran"], a["lens"], a["B"], a["H"], a["D"], a["sc"], a["o"], a["os"],
+                                 a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(wa):
+    for name in ("q", "kc", "vc", "ks", "vs", "lens", "o"):
+        assert _dec(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dec(wa, L=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dec(wa, gran=7) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dec(wa, sc=float("inf")) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dec(wa, D=32) == wa.WA_ERR_UNSUPPORTED
+    assert _dec(wa, kc=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _dec(wa, qs=wa.Strides(20 * 64, 0, 60)) == wa.WA_ERR_UNSUPPORTED
+    # B*H = 6 splits the 1500 keys, so a workspace is required
+    assert _dec(wa, ws=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dec(wa, wsb=64) == wa.WA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_valid_call_without_device_reports_hip_error(wa):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: a valid call with fake pointers would launch")
+    assert _enc(wa) == wa.WA_ERR_HIP

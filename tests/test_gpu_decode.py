@@ -1,0 +1,163 @@
+"""GPU parity of wa_decode_attn against the oracle (max-abs 2e-2, mean-abs 2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attn, quant
+from tests.gpu_helpers import announce, assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gran_id(gran):
+    return quant.PER_TENSOR if gran == "tensor" else quant.PER_HEAD
+
+
+def _gpu_decode(wa, q, kc, vc, ks, vs, lens, gran, kc_dev=None, vc_dev=None, poison=True):
+    qd = to_dev(q)
+    out = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device="cuda") if poison else None
+    kd = kc_dev if kc_dev is not None else to_dev(kc)
+    vd = vc_dev if vc_dev is not None else to_dev(vc)
+    o = wa.wa_decode_attn(qd, kd, vd, to_dev(ks), to_dev(vs), to_dev(np.asarray(lens, np.int32)),
+                          gran, 0.125, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(q, kc, vc, ks, vs, lens, gran, rows=None):
+    qf = q.float().numpy()
+    kcn, vcn = kc.numpy(), vc.numpy()
+    lens = np.asarray(lens)
+    if rows is not None:
+        qf, kcn, vcn, lens = qf[rows], kcn[rows], vcn[rows], lens[rows]
+    return attn.decode_attention(qf, kcn, vcn, ks, vs, _gran_id(gran), lens, 0.125)
+
+
+@pytest.mark.parametrize("which", ["self", "cross"])
+def test_small_workload(gpu, which):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["tiny"]
+    L = cfg["self_len"] if which == "self" else cfg["T"]
+    announce(f"decode small workload {which}: B=1 H=6 L={L}")
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(1, cfg["H"], L, [L], "tensor", 0, which)
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
+    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), f"decode small {which}")
+
+
+def test_large_v3_decode_step_full_size(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["dec_l3"]
+    B, H = cfg["B"], cfg["H"]
+    announce(f"decode large-v3 step: B={B} H={H} cross 1500 + self U[1,448]")
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, 1500, np.full(B, 1500), "tensor", 0, "cross")
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
+    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), "decode large-v3 cross")
+    lens_s = workloads.lens_uniform(B, cfg["self_lo"], cfg["self_hi"], 0)
+    q, kc, vc, ks, vs, lens_s = workloads.decode_inputs(B, H, 448, lens_s, "tensor", 0, "self")
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens_s, "tensor")
+    assert_close(got, _oracle(q, kc, vc, ks, vs, lens_s, "tensor"), "decode large-v3 self")
+
+
+def test_long_audio_batch_full_size_sampled(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["long"]
+    B, H = cfg["B"], cfg["H"]
+    announce(f"decode long-audio batch: B={B} H={H} cross 1500 per-head (sampled rows)")
+    rows = np.random.default_rng(0).choice(B, size=12, replace=False)
+    rows.sort()
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, 1500, np.full(B, 1500), "head", 0, "cross")
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head")
+    assert torch.isfinite(got.float()).all()
+    assert_close(got[torch.as_tensor(rows, device="cuda")], _oracle(q, kc, vc, ks, vs, lens, "head", rows),
+                 "decode long cross (sampled)")
+    lens_s = workloads.lens_zipf(B, cfg["zipf_a"], cfg["cap"], 0)
+    q, kc, vc, ks, vs, lens_s = workloads.decode_inputs(B, H, 448, lens_s, "head", 0, "self")
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens_s, "head")
+    assert_close(got, _oracle(q, kc, vc, ks, vs, lens_s, "head"), "decode long self (all rows)")
+
+
+@pytest.mark.parametrize("B,H,L", [(1, 1, 77), (3, 2, 1), (2, 3, 300), (5, 4, 1500), (300, 8, 65)])
+def test_ragged_edges(gpu, B, H, L):
+    import whisper_attention_amd as wa
+    announce(f"decode ragged edges B={B} H={H} L={L}")
+    g = np.random.default_rng(B * 1000 + L)
+    lens = g.integers(0, L + 1, size=B)
+    lens[0] = L
+    if B > 1:
+        lens[1] = min(1, L)
+    if B > 2:
+        lens[2] = 0
+    for gran in ("tensor", "head"):
+        q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, L, lens, gran, 7, "self")
+        got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, gran)
+        want = _oracle(q, kc, vc, ks, vs, lens, gran)
+        assert_close(got, want, f"decode edges B={B} H={H} L={L} {gran}")
+        zero = np.asarray(lens) == 0
+        assert torch.all(got[torch.as_tensor(zero, device="cuda")].float() == 0)
+
+
+def test_strided_cache_with_guards(gpu):
+    """Caches that are slices of a larger buffer: padding slots hold NaN codes
+    that must never be read."""
+    import whisper_attention_amd as wa
+    announce("decode strided cache with NaN guards beyond each length")
+    B, H, L, Lbuf = 6, 4, 200, 256
+    lens = np.array([200, 1, 77, 150, 199, 64])
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, L, lens, "head", 8, "cross")
+    big_k = torch.full((B, H + 1, Lbuf, 64), 0x7F, dtype=torch.uint8)
+    big_v = torch.full((B, H + 1, Lbuf, 64), 0xFF, dtype=torch.uint8)
+    for b in range(B):
+        big_k[b, :H, :lens[b]] = kc[b, :, :lens[b]]
+        big_v[b, :H, :lens[b]] = vc[b, :, :lens[b]]
+    kd = to_dev(big_k)[:, :H, :L]
+    vd = to_dev(big_v)[:, :H, :L]
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head", kc_dev=kd, vc_dev=vd)
+    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "head"), "decode strided+guards")
+
+
+def test_deterministic(gpu):
+    import whisper_attention_amd as wa
+    announce("decode determinism")
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(4, 6, 1500, [1500, 700, 3, 1], "tensor", 9, "cross")
+    a = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
+    b = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_end_to_end_quantize_then_decode(gpu):
+    """bf16 K/V -> GPU quantize (codes checked bit-exact) -> GPU decode."""
+    import whisper_attention_amd as wa
+    announce("decode end-to-end after GPU quantize, small workload")
+    H, L = 6, 1500
+    k = workloads.bf16_normal((1, L, H, 64), 0, workloads.TID_KV_K)
+    v = workloads.bf16_normal((1, L, H, 64), 0, workloads.TID_KV_V)
+    q = workloads.bf16_normal((1, H, 64), 0, workloads.TID_DQ)
+    caches, scales = [], []
+    for x in (k, v):
+        c = torch.zeros((1, H, L, 64), dtype=torch.uint8, device="cuda")
+        s = torch.zeros(1, dtype=torch.float32, device="cuda")
+        wa.wa_kv_quant_fp8(to_dev(x), c, s, "tensor")
+        caches.append(c)
+        scales.append(s)
+    torch.cuda.synchronize()
+    oc, os_ = [], []
+    for x in (k, v):
+        cache = np.zeros((1, H, L, 64), dtype=np.uint8)
+        os_.append(quant.quantize_kv(x.float().numpy(), [L], [0], cache, quant.PER_TENSOR))
+        oc.append(cache)
+    for i in range(2):
+        assert np.array_equal(caches[i].cpu().numpy(), oc[i])
+        assert scales[i].cpu().numpy().view(np.uint32)[0] == os_[i].view(np.uint32)[0]
+    out = wa.wa_decode_attn(to_dev(q), caches[0], caches[1], scales[0], scales[1],
+                            to_dev(np.array([L], np.int32)), "tensor", 0.125)
+    torch.cuda.synchronize()
+    want = attn.decode_attention(q.float().numpy(), oc[0], oc[1], os_[0], os_[1], quant.PER_TENSOR,
+                                 [L], 0.125)
+    assert_close(out, want, "decode end-to-end")
+    # and against unquantized attention: fp8 storage error only
+    ref = attn.dense_attention(np.concatenate([np.zeros((1, L - 1, H, 64)), q.float().numpy()[:, None]], 1),
+                               k.float().numpy(), v.float().numpy(), [L], False, 0.125)[0, L - 1]
+    err = np.abs(out.float().cpu().numpy()[0] - ref).max()
+    print(f"[info] fp8 KV vs bf16 KV attention max-abs {err:.3e}", flush=True)
+    assert err < 0.1

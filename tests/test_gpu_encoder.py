@@ -1,0 +1,128 @@
+"""GPU parity of wa_encoder_attn against the oracle (max-abs 2e-2, mean-abs 2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attn
+from tests.gpu_helpers import announce, assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+POISON = float("nan")
+
+
+def _gpu(wa, q, k, v, lens, causal, views=None):
+    qd, kd, vd = views if views is not None else (to_dev(q), to_dev(k), to_dev(v))
+    out = torch.full(qd.shape, POISON, dtype=torch.bfloat16, device="cuda")
+    ld = None if lens is None else to_dev(np.asarray(lens, np.int32))
+    wa.wa_encoder_attn(qd, kd, vd, out=out, lens=ld, causal=causal, softmax_scale=0.125)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(got, q, k, v, lens, causal, what, pairs=None):
+    """Compare valid rows; rows at or beyond a length must still hold the poison."""
+    B, T, H, _ = q.shape
+    lens_a = np.full(B, T) if lens is None else np.asarray(lens)
+    g = got.float().cpu().numpy()
+    for b in range(B):
+        assert np.all(np.isnan(g[b, lens_a[b]:])), f"{what}: rows beyond len {lens_a[b]} of seq {b} written"
+    if pairs is None:
+        want = attn.dense_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens_a,
+                                    causal, 0.125)
+        mask = np.arange(T)[None, :] < lens_a[:, None]
+        assert_close(torch.from_numpy(g[mask]), want[mask], what)
+    else:
+        gs, ws = [], []
+        for b, h in pairs:
+            n = lens_a[b]
+            w = attn.dense_attention(q[b:b + 1, :, h:h + 1].float().numpy(), k[b:b + 1, :, h:h + 1].float().numpy(),
+                                     v[b:b + 1, :, h:h + 1].float().numpy(), [n], causal, 0.125)
+            gs.append(g[b, :n, h])
+            ws.append(w[0, :n, 0])
+        assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,T,lens", [(2, 3, 300, [300, 131]), (3, 2, 77, [77, 1, 64]),
+                                        (1, 1, 1, [1]), (2, 2, 129, [0, 129]), (1, 2, 128, [128])])
+def test_ragged_shapes(gpu, B, H, T, lens, causal):
+    import whisper_attention_amd as wa
+    announce(f"encoder ragged B={B} H={H} T={T} lens={lens} causal={causal}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=T)
+    got = _gpu(wa, q, k, v, lens, causal)
+    _check(got, q, k, v, lens, causal, f"encoder B={B} H={H} T={T} causal={causal}")
+
+
+def test_small_workload(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["tiny"]
+    announce("encoder small workload B=1 H=6 T=1500")
+    q, k, v = workloads.encoder_inputs(cfg["B"], cfg["H"], cfg["T"], seed=0)
+    got = _gpu(wa, q, k, v, None, False)
+    _check(got, q, k, v, None, False, "encoder small")
+
+
+def test_large_v3_encoder_full_size_sampled(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["enc_l3"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    announce(f"encoder large-v3 B={B} H={H} T={T} (sampled (b, h))")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=0)
+    got = _gpu(wa, q, k, v, None, False)
+    assert torch.isfinite(got.float()).all()
+    g = np.random.default_rng(1)
+    pairs = [(0, 0), (B - 1, H - 1)] + [(int(g.integers(B)), int(g.integers(H))) for _ in range(6)]
+    _check(got, q, k, v, None, False, "encoder large-v3 (sampled)", pairs=pairs)
+
+
+def test_prefill_causal_full_size(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["prefill"]
+    announce("encoder causal prefill B=128 H=20 T=224 lens U[4,224]")
+    q, k, v, lens = workloads.prefill_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["lo"], cfg["hi"],
+                                             cfg["outlier_p"], cfg["outlier_mult"], seed=0)
+    got = _gpu(wa, q, k, v, lens, True)
+    _check(got, q, k, v, lens, True, "prefill causal")
+
+
+def test_strided_layouts(gpu):
+    """Q/K/V stored [B][H][T][64] and passed as [B][T][H][64] views."""
+    import whisper_attention_amd as wa
+    announce("encoder strided [B][H][T][64] storage")
+    B, H, T = 2, 3, 200
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=11)
+    views = tuple(to_dev(t.permute(0, 2, 1, 3).contiguous()).permute(0, 2, 1, 3) for t in (q, k, v))
+    got = _gpu(wa, q, k, v, [200, 150], False, views=views)
+    _check(got, q, k, v, [200, 150], False, "encoder strided")
+
+
+def test_softmax_invariants_on_gpu(gpu):
+    """Equal keys -> mean of V; one dominant key -> its V row."""
+    import whisper_attention_amd as wa
+    announce("encoder softmax invariants")
+    T, H = 200, 2
+    g = np.random.default_rng(12)
+    q = torch.from_numpy(g.standard_normal((1, T, H, 64)).astype(np.float32)).to(torch.bfloat16)
+    krow = torch.from_numpy(g.standard_normal(64).astype(np.float32)).to(torch.bfloat16)
+    k = krow.expand(1, T, H, 64).contiguous()
+    v = torch.from_numpy(g.standard_normal((1, T, H, 64)).astype(np.float32)).to(torch.bfloat16)
+    got = _gpu(wa, q, k, v, None, False).float().cpu().numpy()
+    mean_v = v.float().numpy().mean(axis=1, keepdims=True)
+    assert np.abs(got - mean_v).max() < 2e-2
+    k2 = torch.zeros((1, T, H, 64), dtype=torch.bfloat16)
+    k2[0, 37, :, 0] = 64.0
+    q2 = torch.zeros((1, T, H, 64), dtype=torch.bfloat16)
+    q2[..., 0] = 8.0                                 # score 64 * 8 / 8 = 64 vs 0
+    got = _gpu(wa, q2, k2, v, None, False).float().cpu().numpy()
+    assert np.abs(got - v.float().numpy()[:, 37:38]).max() < 1e-2
+
+
+def test_deterministic(gpu):
+    import whisper_attention_amd as wa
+    announce("encoder determinism")
+    q, k, v = workloads.encoder_inputs(2, 4, 700, seed=13)
+    a = _gpu(wa, q, k, v, [700, 333], True)
+    b = _gpu(wa, q, k, v, [700, 333], True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -1,0 +1,190 @@
+"""Python binding of libwa.so, the C-ABI library of the Whisper attention hot path.
+
+Argument marshalling only: every step runs in the HIP kernels behind
+``include/wa.h``.  PyTorch provides device memory and the current stream.
+The functions keep the C names:
+
+* ``wa_kv_quant_fp8``  bf16 -> E4M3 KV-cache fill with dynamic or static scales
+* ``wa_encoder_attn``  dense bf16 attention (encoder, or causal prompt prefill)
+* ``wa_decode_attn``   one query token per sequence against an E4M3 cache
+
+The library must have been built (``python -m whisper_attention_amd.build``);
+importing fails loudly when it is missing -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwa.so")
+
+WA_OK = 0
+WA_ERR_INVALID_ARGUMENT = 1
+WA_ERR_UNSUPPORTED = 2
+WA_ERR_WORKSPACE_TOO_SMALL = 3
+WA_ERR_HIP = 4
+
+WA_SCALE_PER_TENSOR = 0
+WA_SCALE_PER_HEAD = 1
+
+HEAD_DIM = 64
+
+
+class Strides(ctypes.Structure):
+    """wa_strides: element strides of the batch, position and head axes."""
+    _fields_ = [("b", ctypes.c_int64), ("t", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+class WaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m whisper_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S, F, Z = ctypes.c_void_p, ctypes.c_int, Strides, ctypes.c_float, ctypes.c_size_t
+    lib.wa_kv_quant_fp8.argtypes = [P, S, I, I, I, I, P, P, P, S, I, P, I, I, P, Z, P]
+    lib.wa_kv_quant_fp8.restype = I
+    lib.wa_kv_quant_fp8_workspace_size.argtypes = [I, I, I, I]
+    lib.wa_kv_quant_fp8_workspace_size.restype = Z
+    lib.wa_encoder_attn.argtypes = [P, S, P, S, P, S, P, S, I, I, I, I, P, I, F, P]
+    lib.wa_encoder_attn.restype = I
+    lib.wa_decode_attn.argtypes = [P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
+    lib.wa_decode_attn.restype = I
+    lib.wa_decode_attn_workspace_size.argtypes = [I, I, I]
+    lib.wa_decode_attn_workspace_size.restype = Z
+    lib.wa_status_string.argtypes = [I]
+    lib.wa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn",
+            "wa_decode_attn", "wa_decode_attn_workspace_size", "wa_status_string")
+
+
+def wa_status_string(status):
+    return lib.wa_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != WA_OK:
+        raise WaError(status, wa_status_string(status))
+
+
+def _gran(g):
+    if g in ("tensor", WA_SCALE_PER_TENSOR):
+        return WA_SCALE_PER_TENSOR
+    if g in ("head", WA_SCALE_PER_HEAD):
+        return WA_SCALE_PER_HEAD
+    raise ValueError(f"scale granularity {g!r}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _act_strides(t):
+    """[B][T][H][D] tensor -> wa_strides(b, t, h)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B][T][H][64] tensor with a contiguous last axis")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _cache_strides(t):
+    """[B][H][L][D] cache -> wa_strides(b, t=slot, h)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B][H][L][64] cache with a contiguous last axis")
+    return Strides(t.stride(0), t.stride(2), t.stride(1))
+
+
+def _tok_strides(t):
+    """[B][H][D] token tensor -> wa_strides(b, 0, h)."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [B][H][64] tensor with a contiguous last axis")
+    return Strides(t.stride(0), 0, t.stride(1))
+
+
+def _bits(t, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t
+
+
+def wa_kv_quant_fp8_workspace_size(B, H, T_max, gran):
+    return int(lib.wa_kv_quant_fp8_workspace_size(B, H, T_max, _gran(gran)))
+
+
+def wa_decode_attn_workspace_size(B, H, cache_len):
+    return int(lib.wa_decode_attn_workspace_size(B, H, cache_len))
+
+
+def wa_kv_quant_fp8(x, cache, scale, gran, lens=None, dst_start=None, compute_scale=True,
+                    workspace=None, stream=None):
+    """Quantize bf16 ``x`` [B][T][H][64] into the uint8 E4M3 ``cache`` [B][H][L][64].
+
+    ``scale`` (float32, [1] or [H]) is written when ``compute_scale`` and read
+    otherwise.  ``lens``/``dst_start`` are int32 device tensors [B] or None.
+    """
+    _bits(x, torch.bfloat16)
+    _bits(cache, torch.uint8)
+    _bits(scale, torch.float32)
+    B, T, H, D = x.shape
+    g = _gran(gran)
+    if workspace is None and compute_scale:
+        n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wa_kv_quant_fp8(_ptr(x), _act_strides(x), B, H, T, D, _ptr(lens), _ptr(dst_start),
+                               _ptr(cache), _cache_strides(cache), cache.shape[2], _ptr(scale), g,
+                               int(bool(compute_scale)), _ptr(workspace), ws_bytes,
+                               _stream(x, stream)))
+    return scale
+
+
+def wa_encoder_attn(q, k, v, out=None, lens=None, causal=False, softmax_scale=0.125, stream=None):
+    """Dense bf16 attention over [B][T][H][64] tensors; returns ``out``."""
+    for t in (q, k, v):
+        _bits(t, torch.bfloat16)
+    B, T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.wa_encoder_attn(_ptr(q), _act_strides(q), _ptr(k), _act_strides(k), _ptr(v),
+                               _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
+                               _ptr(lens), int(bool(causal)), float(softmax_scale),
+                               _stream(q, stream)))
+    return out
+
+
+def wa_decode_attn(q, k_cache, v_cache, k_scale, v_scale, lens, gran, softmax_scale=0.125,
+                   out=None, workspace=None, stream=None):
+    """One query token per (b, h): q [B][H][64] bf16 against uint8 caches [B][H][L][64]."""
+    _bits(q, torch.bfloat16)
+    _bits(k_cache, torch.uint8)
+    _bits(v_cache, torch.uint8)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    B, H, D = q.shape
+    L = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = wa_decode_attn_workspace_size(B, H, L)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wa_decode_attn(_ptr(q), _tok_strides(q), _ptr(k_cache), _ptr(v_cache),
+                              _cache_strides(k_cache), L, _ptr(k_scale), _ptr(v_scale),
+                              _gran(gran), _ptr(lens), B, H, D, float(softmax_scale), _ptr(out),
+                              _tok_strides(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out

@@ -1,0 +1,143 @@
+// Host entry points of the C ABI declared in include/wa.h: argument checks
+// (before any HIP call), the gfx950 check, plan/workspace sizing and the
+// kernel launches.  No device memory is allocated here.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "wa_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool bf16_layout_ok(const void *p, wa_strides s) {
+  return aligned16(p) && s.b % 8 == 0 && s.t % 8 == 0 && s.h % 8 == 0;
+}
+bool u8_layout_ok(const void *p, wa_strides s) {
+  return aligned16(p) && s.b % 16 == 0 && s.t % 16 == 0 && s.h % 16 == 0;
+}
+
+// The first call on each device checks that it is a gfx950.
+constexpr int kMaxDevices = 64;
+std::once_flag g_arch_once[kMaxDevices];
+int g_arch_ok[kMaxDevices];
+
+wa_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return WA_ERR_HIP;
+  if (dev >= kMaxDevices) return WA_ERR_UNSUPPORTED;
+  std::call_once(g_arch_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_arch_ok[dev] = -1;
+      return;
+    }
+    g_arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  if (g_arch_ok[dev] < 0) return WA_ERR_HIP;
+  return g_arch_ok[dev] ? WA_OK : WA_ERR_UNSUPPORTED;
+}
+
+wa_status from_hip(hipError_t e) { return e == hipSuccess ? WA_OK : WA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *wa_status_string(wa_status s) {
+  switch (s) {
+    case WA_OK: return "WA_OK";
+    case WA_ERR_INVALID_ARGUMENT: return "WA_ERR_INVALID_ARGUMENT: null pointer, non-positive size or bad enum";
+    case WA_ERR_UNSUPPORTED: return "WA_ERR_UNSUPPORTED: head_dim != 64, misaligned pointer/stride, or device is not gfx950";
+    case WA_ERR_WORKSPACE_TOO_SMALL: return "WA_ERR_WORKSPACE_TOO_SMALL";
+    case WA_ERR_HIP: return "WA_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown wa_status";
+}
+
+size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gran) {
+  if (B <= 0 || H <= 0 || T_max <= 0) return 0;
+  return wa::quant_workspace_bytes(wa::quant_plan(B, H, T_max, gran));
+}
+
+wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                          int head_dim, const int32_t *lens, const int32_t *dst_start,
+                          uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                          wa_scale_gran gran, int compute_scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !cache || !scale) return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || T_max <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (compute_scale != 0 && compute_scale != 1) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  if (!bf16_layout_ok(x, xs) || !u8_layout_ok(cache, cs)) return WA_ERR_UNSUPPORTED;
+  const wa::QuantPlan plan = wa::quant_plan(B, H, T_max, gran);
+  if (compute_scale) {
+    if (!workspace) return WA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(workspace)) return WA_ERR_UNSUPPORTED;
+    if (workspace_bytes < wa::quant_workspace_bytes(plan)) return WA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_kv_quant(x, xs, B, H, T_max, lens, dst_start, cache, cs, cache_len,
+                                      scale, gran == WA_SCALE_PER_HEAD, compute_scale,
+                                      static_cast<uint32_t *>(workspace), plan, stream));
+}
+
+wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+                          const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
+                          int H, int T_max, int head_dim, const int32_t *lens, int causal,
+                          float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o) return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || T_max <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return WA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  if (!bf16_layout_ok(q, qs) || !bf16_layout_ok(k, ks) || !bf16_layout_ok(v, vs) ||
+      !bf16_layout_ok(o, os))
+    return WA_ERR_UNSUPPORTED;
+  if ((long)B * H * ((T_max + 127) / 128) > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
+                                     softmax_scale, stream));
+}
+
+size_t wa_decode_attn_workspace_size(int B, int H, int cache_len) {
+  if (B <= 0 || H <= 0 || cache_len <= 0) return 0;
+  return wa::decode_workspace_bytes(B, H, wa::decode_plan(B, H, cache_len));
+}
+
+wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                         const uint8_t *v_cache, wa_strides cs, int cache_len,
+                         const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                         const int32_t *lens, int B, int H, int head_dim, float softmax_scale,
+                         uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !lens || !o)
+    return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  wa_strides qs2 = {qs.b, 0, qs.h}, os2 = {os.b, 0, os.h};
+  if (!bf16_layout_ok(q, qs2) || !bf16_layout_ok(o, os2) || !u8_layout_ok(k_cache, cs) ||
+      !u8_layout_ok(v_cache, cs))
+    return WA_ERR_UNSUPPORTED;
+  const wa::DecodePlan plan = wa::decode_plan(B, H, cache_len);
+  if ((long)B * H * plan.n_split > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  const size_t need = wa::decode_workspace_bytes(B, H, plan);
+  if (need > 0) {
+    if (!workspace) return WA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(workspace)) return WA_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return WA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_decode(q, qs2, k_cache, v_cache, cs, cache_len, k_scale, v_scale,
+                                    gran == WA_SCALE_PER_HEAD, lens, B, H, softmax_scale, o, os2,
+                                    static_cast<float *>(workspace), plan, stream));
+}
+
+}  // extern "C"

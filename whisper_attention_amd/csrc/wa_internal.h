@@ -1,0 +1,49 @@
+// Internal declarations shared by the wa_* host entry points and the kernel
+// launchers.  gfx950 (CDNA4) only: wave64, MFMA 32x32x16 bf16, OCP fp8
+// conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wa.h"
+
+namespace wa {
+
+// ---- kv quantize --------------------------------------------------------
+struct QuantPlan {
+  int pieces_per_row;   // H * 8: one piece = 8 bf16 = 16 bytes
+  int groups;           // 1 (per tensor) or H (per head)
+  int amax_blocks;      // blocks of the abs-max pass
+  int encode_blocks;    // blocks of the encode pass
+};
+QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran);
+size_t quant_workspace_bytes(const QuantPlan &p);
+
+hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                           const int32_t *lens, const int32_t *dst_start, uint8_t *cache,
+                           wa_strides cs, int cache_len, float *scale, int per_head,
+                           int compute_scale, uint32_t *ws, const QuantPlan &plan,
+                           hipStream_t stream);
+
+// ---- decode attention ---------------------------------------------------
+struct DecodePlan {
+  int n_split;          // key chunks per (b, h)
+  int chunk;            // keys per chunk (multiple of 64)
+};
+DecodePlan decode_plan(int B, int H, int cache_len);
+size_t decode_workspace_bytes(int B, int H, const DecodePlan &p);
+
+hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, const uint8_t *vc,
+                         wa_strides cs, int cache_len, const float *k_scale,
+                         const float *v_scale, int per_head, const int32_t *lens, int B, int H,
+                         float softmax_scale, uint16_t *o, wa_strides os, float *ws,
+                         const DecodePlan &plan, hipStream_t stream);
+
+// ---- encoder / prefill attention ----------------------------------------
+hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+                          const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
+                          int H, int T_max, const int32_t *lens, int causal,
+                          float softmax_scale, hipStream_t stream);
+
+}  // namespace wa

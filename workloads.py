@@ -59,22 +59,37 @@ def lens_zipf(B, a, cap, seed, tid=TID_LENS):
     return np.minimum(rng(seed, tid).zipf(a, size=B), cap).astype(np.int32)
 
 
-def fp8_codes(shape, seed, tid):
-    """Synthetic E4M3 cache bytes shaped like a quantized bell curve.
+def _fp8_byte_map():
+    """256-entry map from a uniform random byte to a synthetic E4M3 code.
 
-    Drawn directly as bytes -- sign uniform, exponent field 15 - k with k
-    geometric (half the mass in the top binade), mantissa uniform -- and never
-    a NaN pattern (exponent 15 with mantissa 7 becomes mantissa 6).  Used
-    where a cache is an input in its own right; codes produced by quantizing
-    bf16 data come from the quantize step itself.
+    Bit 0 is the sign, bits 1-3 the mantissa, and the top four bits pick how
+    many binades below the top one the exponent field sits: 0 for half of
+    them, 1 for a quarter, 2 for an eighth, 3 and 4 for a sixteenth each.
+    Exponent 15 with mantissa 7 (NaN) becomes mantissa 6.
     """
-    g = rng(seed, tid)
-    sign = g.integers(0, 2, size=shape, dtype=np.uint8)
-    k = np.minimum(g.geometric(0.5, size=shape) - 1, 15).astype(np.uint8)
-    e = (15 - k).astype(np.uint8)
-    m = g.integers(0, 8, size=shape, dtype=np.uint8)
-    m = np.where((e == 15) & (m == 7), np.uint8(6), m)
-    return torch.from_numpy(((sign << 7) | (e << 3) | m).astype(np.uint8))
+    drop = [0] * 8 + [1] * 4 + [2] * 2 + [3] + [4]
+    out = np.zeros(256, dtype=np.uint8)
+    for r in range(256):
+        sign, m, e = r & 1, (r >> 1) & 7, 15 - drop[r >> 4]
+        if e == 15 and m == 7:
+            m = 6
+        out[r] = (sign << 7) | (e << 3) | m
+    return out
+
+
+_FP8_BYTE_MAP = _fp8_byte_map()
+
+
+def fp8_codes(shape, seed, tid):
+    """Synthetic E4M3 cache bytes shaped like a quantized bell curve (uint8 CPU tensor).
+
+    Uniform random bytes sent through a fixed 256-entry map: magnitudes
+    concentrate in the top binades as codes of a quantized Gaussian do, and
+    no NaN pattern occurs.  Used where a cache is an input in its own right;
+    codes produced by quantizing bf16 data come from the quantize step.
+    """
+    r = rng(seed, tid).integers(0, 256, size=shape, dtype=np.uint8)
+    return torch.from_numpy(_FP8_BYTE_MAP[r])
 
 
 def scales_uniform(n, seed, tid, lo=2.0 / 448, hi=6.0 / 448):
