@@ -1,0 +1,261 @@
+"""Throughput of the Whisper attention hot path on one MI355X.
+
+One step is one pass of every kernel of the path over one batch of synthetic,
+seeded inputs already resident in HBM, at the large-v3 shapes:
+
+  1. encoder self-attention   B=16 chunks x 1500 frames, 20 heads, bf16 MFMA
+  2. KV quantize (cache fill) B=128 prompts, lengths U[4,224], per-head E4M3
+                              scales, K and V (1% x20 outliers)
+  3. prompt prefill attention the same 128 prompts, causal
+  4. decode step              B=64 sequences, one token each: cross-attention
+                              over 1500 fp8 frames and self-attention over an
+                              fp8 cache of length U[1,448]
+
+``value`` is the encoder attention throughput in TFLOP/s (4*B*H*T^2*64
+algorithmic flops per call over the call's average duration, measured with
+HIP events on the launch stream); the decode throughput in GB/s (algorithmic
+bytes: every cached K/V byte read once plus q and o) sits beside it, each
+with its fraction of the MI355X peak.  ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the encoder workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+HEAD_DIM = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def gen_bf16(shape, gen, outlier_p=0.0):
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    if outlier_p > 0:
+        m = torch.rand(shape, generator=gen, device="cuda") < outlier_p
+        x = torch.where(m, x * 20.0, x)
+    return x.to(torch.bfloat16)
+
+
+class Workload:
+    """Device-resident inputs, outputs and workspaces of one step."""
+
+    def __init__(self, seed=0):
+        import whisper_attention_amd as wa
+        import workloads
+        self.wa = wa
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        dev = torch.device("cuda")
+        # 1. encoder
+        self.enc = dict(B=16, H=20, T=1500)
+        B, H, T = self.enc["B"], self.enc["H"], self.enc["T"]
+        self.qe, self.ke, self.ve = (gen_bf16((B, T, H, HEAD_DIM), g) for _ in range(3))
+        self.oe = torch.empty_like(self.qe)
+        # 2./3. prefill + cache fill
+        self.pre = dict(B=128, H=20, T=224)
+        B, H, T = self.pre["B"], self.pre["H"], self.pre["T"]
+        self.lens_p_host = workloads.lens_uniform(B, 4, 224, seed)
+        self.lens_p = torch.from_numpy(self.lens_p_host).to(dev)
+        self.qp = gen_bf16((B, T, H, HEAD_DIM), g)
+        self.kp = gen_bf16((B, T, H, HEAD_DIM), g, 0.01)
+        self.vp = gen_bf16((B, T, H, HEAD_DIM), g, 0.01)
+        self.op = torch.empty_like(self.qp)
+        self.kcp = torch.zeros((B, H, T, HEAD_DIM), dtype=torch.uint8, device=dev)
+        self.vcp = torch.zeros_like(self.kcp)
+        self.ksp = torch.zeros(H, dtype=torch.float32, device=dev)
+        self.vsp = torch.zeros(H, dtype=torch.float32, device=dev)
+        self.ws_q = torch.empty(max(16, wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head")),
+                                dtype=torch.uint8, device=dev)
+        # 4. decode step: caches filled once (untimed) by the quantize kernel
+        self.dec = dict(B=64, H=20, Lx=1500, Ls=448)
+        B, H, Lx, Ls = self.dec["B"], self.dec["H"], self.dec["Lx"], self.dec["Ls"]
+        self.lens_s_host = workloads.lens_uniform(B, 1, Ls, seed)
+        self.lens_s = torch.from_numpy(self.lens_s_host).to(dev)
+        self.lens_x = torch.full((B,), Lx, dtype=torch.int32, device=dev)
+        self.qd = gen_bf16((B, H, HEAD_DIM), g)
+        self.od_x = torch.empty_like(self.qd)
+        self.od_s = torch.empty_like(self.qd)
+        self.xk, self.xv, self.sk, self.sv = [], [], [], []
+        caches = {}
+        for name, L, lens in (("x", Lx, None), ("s", Ls, self.lens_s)):
+            for kv in ("k", "v"):
+                src = gen_bf16((B, L, H, HEAD_DIM), g)
+                c = torch.zeros((B, H, L, HEAD_DIM), dtype=torch.uint8, device=dev)
+                s = torch.zeros(1, dtype=torch.float32, device=dev)
+                wa.wa_kv_quant_fp8(src, c, s, "tensor", lens=lens)
+                caches[name + kv] = (c, s)
+                del src
+        self.caches = caches
+        self.ws_dx = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)),
+                                 dtype=torch.uint8, device=dev)
+        self.ws_ds = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)),
+                                 dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # algorithmic work per call
+    def enc_flops(self):
+        e = self.enc
+        return 4.0 * e["B"] * e["H"] * e["T"] ** 2 * HEAD_DIM
+
+    def prefill_flops(self):
+        L = self.lens_p_host.astype(np.float64)
+        return float(np.sum(4.0 * self.pre["H"] * HEAD_DIM * L * (L + 1) / 2))
+
+    def quant_bytes(self):
+        # per valid element: 2 bytes read + 1 byte written, K and V each
+        n = float(self.lens_p_host.sum()) * self.pre["H"] * HEAD_DIM
+        return 2 * 3.0 * n
+
+    def decode_bytes(self):
+        d = self.dec
+        qo = 2 * 2.0 * d["B"] * d["H"] * HEAD_DIM
+        cross = 2.0 * d["B"] * d["H"] * d["Lx"] * HEAD_DIM + qo
+        self_ = 2.0 * float(self.lens_s_host.sum()) * d["H"] * HEAD_DIM + qo
+        return cross, self_
+
+    def run(self, ev=None):
+        """One step; ``ev`` (list of 7 events) brackets the kernels."""
+        wa = self.wa
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        wa.wa_encoder_attn(self.qe, self.ke, self.ve, out=self.oe, softmax_scale=0.125)
+        rec(1)
+        wa.wa_kv_quant_fp8(self.kp, self.kcp, self.ksp, "head", lens=self.lens_p, workspace=self.ws_q)
+        wa.wa_kv_quant_fp8(self.vp, self.vcp, self.vsp, "head", lens=self.lens_p, workspace=self.ws_q)
+        rec(2)
+        wa.wa_encoder_attn(self.qp, self.kp, self.vp, out=self.op, lens=self.lens_p, causal=True,
+                           softmax_scale=0.125)
+        rec(3)
+        (xk, xks), (xv, xvs) = self.caches["xk"], self.caches["xv"]
+        wa.wa_decode_attn(self.qd, xk, xv, xks, xvs, self.lens_x, "tensor", 0.125, out=self.od_x,
+                          workspace=self.ws_dx)
+        rec(4)
+        (sk, sks), (sv, svs) = self.caches["sk"], self.caches["sv"]
+        wa.wa_decode_attn(self.qd, sk, sv, sks, svs, self.lens_s, "tensor", 0.125, out=self.od_s,
+                          workspace=self.ws_ds)
+        rec(5)
+
+
+def cpu_baseline(budget_s):
+    """The CPU oracle on a bounded sample of the encoder workload: whole
+    (b, h) pairs of B=16 x H=20 x T=1500 until ``budget_s`` seconds pass."""
+    import workloads
+    from oracle import attn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = 1500
+    q, k, v = workloads.encoder_inputs(1, 4, T, seed=0)
+    qf, kf, vf = (t.float().numpy() for t in (q, k, v))
+    attn.dense_attention(qf[:, :64, :1], kf[:, :64, :1], vf[:, :64, :1], [64], False, 0.125)  # warm
+    done, t0 = 0, time.perf_counter()
+    while True:
+        h = done % 4
+        attn.dense_attention(qf[:, :, h:h + 1], kf[:, :, h:h + 1], vf[:, :, h:h + 1], [T], False, 0.125)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 64:
+            break
+    flops = done * 4.0 * T * T * HEAD_DIM
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole (b, h) pairs of the encoder workload (T=1500, D=64), float64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "requested_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] setting up inputs (steps={args.steps} warmup={args.warmup})", file=sys.stderr, flush=True)
+    wl = Workload(seed=0)
+    for _ in range(args.warmup):
+        wl.run()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("[bench] timed steps done", file=sys.stderr, flush=True)
+
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
+    ms = seg.mean(axis=0)          # per-part average ms
+    ms_step = wall * 1e3 / args.steps
+    enc_tflops = wl.enc_flops() / (ms[0] * 1e-3) / 1e12
+    quant_gbps = wl.quant_bytes() / (ms[1] * 1e-3) / 1e9
+    pre_tflops = wl.prefill_flops() / (ms[2] * 1e-3) / 1e12
+    bx, bs = wl.decode_bytes()
+    dec_gbps = (bx + bs) / ((ms[3] + ms[4]) * 1e-3) / 1e9
+    cross_gbps = bx / (ms[3] * 1e-3) / 1e9
+    self_gbps = bs / (ms[4] * 1e-3) / 1e9
+
+    rec = {
+        "metric": "encoder attn TFLOP/s (% bf16 MFMA peak) + fp8 decode attn GB/s (% HBM peak)",
+        "value": round(enc_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; fp8 caches filled by the quantize kernel)",
+        "config": {"workload": "large-v3 attention step: encoder B=16 T=1500 H=20 D=64 non-causal; "
+                               "decode B=64 H=20 cross 1500 + self U[1,448] fp8 per-tensor; "
+                               "prefill B=128 H=20 U[4,224] causal + per-head fp8 cache fill",
+                   "encoder": wl.enc, "decode": wl.dec, "prefill": wl.pre},
+        "decode_attn": {"value": round(dec_gbps, 1), "unit": "GB/s",
+                        "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                        "cross_GBps": round(cross_gbps, 1), "self_GBps": round(self_gbps, 1),
+                        "us": [round(ms[3] * 1e3, 2), round(ms[4] * 1e3, 2)]},
+        "encoder_attn": {"value": round(enc_tflops, 2), "unit": "TFLOP/s",
+                         "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4), "us": round(ms[0] * 1e3, 2)},
+        "kv_quant": {"value": round(quant_gbps, 1), "unit": "GB/s",
+                     "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
+                     "note": "two calls (K and V), each two kernels"},
+        "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
+        "roofline": {"bound": "mfma", "kernel": "encoder_attn_kernel",
+                     "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,16 +28,19 @@ import numpy as np
 from . import quant
 
 
-def dense_attention(q, k, v, lens, causal, softmax_scale):
+def dense_attention(q, k, v, lens, causal, softmax_scale, with_magnitude=False):
     """q, k, v: [B][T][H][D] (bf16 values as float) -> O float64 [B][T][H][D].
 
-    Rows i >= lens[b] are NaN.
+    Rows i >= lens[b] are NaN.  With ``with_magnitude`` also returns
+    sum_j p_j |V[j]| / sum_j p_j, the size of the terms each output sums
+    (rounding the weights p by a relative e moves O by at most e times it).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, T, H, D = q.shape
     out = np.full((B, T, H, D), np.nan, dtype=np.float64)
+    mag = np.full((B, T, H, D), np.nan, dtype=np.float64) if with_magnitude else None
     for b in range(B):
         n = int(lens[b])
         if n == 0:
@@ -52,17 +55,21 @@ def dense_attention(q, k, v, lens, causal, softmax_scale):
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
             out[b, :n, h, :] = (p @ vb) / p.sum(axis=1, keepdims=True)
-    return out
+            if with_magnitude:
+                mag[b, :n, h, :] = (p @ np.abs(vb)) / p.sum(axis=1, keepdims=True)
+    return (out, mag) if with_magnitude else out
 
 
-def decode_attention_dequant(q, khat, vhat, lens, softmax_scale):
+def decode_attention_dequant(q, khat, vhat, lens, softmax_scale, with_magnitude=False):
     """One query per (b, h) against already-dequantized keys and values.
 
-    q: [B][H][D]; khat, vhat: [B][H][L][D] float; lens: [B].  -> [B][H][D] float64.
+    q: [B][H][D]; khat, vhat: [B][H][L][D] float; lens: [B].  -> [B][H][D] float64
+    (plus sum_j p_j |V^_j| / sum_j p_j with ``with_magnitude``).
     """
     q = np.asarray(q, dtype=np.float64)
     B, H, D = q.shape
     out = np.zeros((B, H, D), dtype=np.float64)
+    mag = np.zeros((B, H, D), dtype=np.float64)
     for b in range(B):
         n = int(lens[b])
         if n == 0:
@@ -73,10 +80,12 @@ def decode_attention_dequant(q, khat, vhat, lens, softmax_scale):
             s = softmax_scale * (kb @ q[b, h])   # [n]
             p = np.exp(s - s.max())
             out[b, h] = (p @ vb) / p.sum()
-    return out
+            mag[b, h] = (p @ np.abs(vb)) / p.sum()
+    return (out, mag) if with_magnitude else out
 
 
-def decode_attention(q, k_cache, v_cache, k_scale, v_scale, gran, lens, softmax_scale):
+def decode_attention(q, k_cache, v_cache, k_scale, v_scale, gran, lens, softmax_scale,
+                     with_magnitude=False):
     """One query token per (b, h) against the fp8 KV cache.
 
     k_cache, v_cache: uint8 codes [B][H][L][D]; k_scale, v_scale: float32 [1]
@@ -85,7 +94,7 @@ def decode_attention(q, k_cache, v_cache, k_scale, v_scale, gran, lens, softmax_
     """
     khat = quant.dequantize(k_cache, k_scale, gran, head_axis=1)
     vhat = quant.dequantize(v_cache, v_scale, gran, head_axis=1)
-    return decode_attention_dequant(q, khat, vhat, lens, softmax_scale)
+    return decode_attention_dequant(q, khat, vhat, lens, softmax_scale, with_magnitude)
 
 
 def decode_partial(q, kb, vb, softmax_scale):

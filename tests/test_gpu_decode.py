@@ -31,7 +31,12 @@ def _oracle(q, kc, vc, ks, vs, lens, gran, rows=None):
     lens = np.asarray(lens)
     if rows is not None:
         qf, kcn, vcn, lens = qf[rows], kcn[rows], vcn[rows], lens[rows]
-    return attn.decode_attention(qf, kcn, vcn, ks, vs, _gran_id(gran), lens, 0.125)
+    return attn.decode_attention(qf, kcn, vcn, ks, vs, _gran_id(gran), lens, 0.125, with_magnitude=True)
+
+
+def _close(got, ora, what):
+    want, mag = ora
+    return assert_close(got, want, what, mag=mag)
 
 
 @pytest.mark.parametrize("which", ["self", "cross"])
@@ -42,7 +47,7 @@ def test_small_workload(gpu, which):
     announce(f"decode small workload {which}: B=1 H=6 L={L}")
     q, kc, vc, ks, vs, lens = workloads.decode_inputs(1, cfg["H"], L, [L], "tensor", 0, which)
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
-    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), f"decode small {which}")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), f"decode small {which}")
 
 
 def test_large_v3_decode_step_full_size(gpu):
@@ -52,11 +57,11 @@ def test_large_v3_decode_step_full_size(gpu):
     announce(f"decode large-v3 step: B={B} H={H} cross 1500 + self U[1,448]")
     q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, 1500, np.full(B, 1500), "tensor", 0, "cross")
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "tensor")
-    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), "decode large-v3 cross")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens, "tensor"), "decode large-v3 cross")
     lens_s = workloads.lens_uniform(B, cfg["self_lo"], cfg["self_hi"], 0)
     q, kc, vc, ks, vs, lens_s = workloads.decode_inputs(B, H, 448, lens_s, "tensor", 0, "self")
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens_s, "tensor")
-    assert_close(got, _oracle(q, kc, vc, ks, vs, lens_s, "tensor"), "decode large-v3 self")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens_s, "tensor"), "decode large-v3 self")
 
 
 def test_long_audio_batch_full_size_sampled(gpu):
@@ -69,12 +74,12 @@ def test_long_audio_batch_full_size_sampled(gpu):
     q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, 1500, np.full(B, 1500), "head", 0, "cross")
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head")
     assert torch.isfinite(got.float()).all()
-    assert_close(got[torch.as_tensor(rows, device="cuda")], _oracle(q, kc, vc, ks, vs, lens, "head", rows),
+    _close(got[torch.as_tensor(rows, device="cuda")], _oracle(q, kc, vc, ks, vs, lens, "head", rows),
                  "decode long cross (sampled)")
     lens_s = workloads.lens_zipf(B, cfg["zipf_a"], cfg["cap"], 0)
     q, kc, vc, ks, vs, lens_s = workloads.decode_inputs(B, H, 448, lens_s, "head", 0, "self")
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens_s, "head")
-    assert_close(got, _oracle(q, kc, vc, ks, vs, lens_s, "head"), "decode long self (all rows)")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens_s, "head"), "decode long self (all rows)")
 
 
 @pytest.mark.parametrize("B,H,L", [(1, 1, 77), (3, 2, 1), (2, 3, 300), (5, 4, 1500), (300, 8, 65)])
@@ -91,8 +96,7 @@ def test_ragged_edges(gpu, B, H, L):
     for gran in ("tensor", "head"):
         q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, L, lens, gran, 7, "self")
         got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, gran)
-        want = _oracle(q, kc, vc, ks, vs, lens, gran)
-        assert_close(got, want, f"decode edges B={B} H={H} L={L} {gran}")
+        _close(got, _oracle(q, kc, vc, ks, vs, lens, gran), f"decode edges B={B} H={H} L={L} {gran}")
         zero = np.asarray(lens) == 0
         assert torch.all(got[torch.as_tensor(zero, device="cuda")].float() == 0)
 
@@ -113,7 +117,7 @@ def test_strided_cache_with_guards(gpu):
     kd = to_dev(big_k)[:, :H, :L]
     vd = to_dev(big_v)[:, :H, :L]
     got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head", kc_dev=kd, vc_dev=vd)
-    assert_close(got, _oracle(q, kc, vc, ks, vs, lens, "head"), "decode strided+guards")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens, "head"), "decode strided+guards")
 
 
 def test_deterministic(gpu):
@@ -152,9 +156,9 @@ def test_end_to_end_quantize_then_decode(gpu):
     out = wa.wa_decode_attn(to_dev(q), caches[0], caches[1], scales[0], scales[1],
                             to_dev(np.array([L], np.int32)), "tensor", 0.125)
     torch.cuda.synchronize()
-    want = attn.decode_attention(q.float().numpy(), oc[0], oc[1], os_[0], os_[1], quant.PER_TENSOR,
-                                 [L], 0.125)
-    assert_close(out, want, "decode end-to-end")
+    want, mag = attn.decode_attention(q.float().numpy(), oc[0], oc[1], os_[0], os_[1], quant.PER_TENSOR,
+                                      [L], 0.125, with_magnitude=True)
+    assert_close(out, want, "decode end-to-end", mag=mag)
     # and against unquantized attention: fp8 storage error only
     ref = attn.dense_attention(np.concatenate([np.zeros((1, L - 1, H, 64)), q.float().numpy()[:, None]], 1),
                                k.float().numpy(), v.float().numpy(), [L], False, 0.125)[0, L - 1]

@@ -29,19 +29,22 @@ def _check(got, q, k, v, lens, causal, what, pairs=None):
     for b in range(B):
         assert np.all(np.isnan(g[b, lens_a[b]:])), f"{what}: rows beyond len {lens_a[b]} of seq {b} written"
     if pairs is None:
-        want = attn.dense_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens_a,
-                                    causal, 0.125)
+        want, mag = attn.dense_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), lens_a,
+                                         causal, 0.125, with_magnitude=True)
         mask = np.arange(T)[None, :] < lens_a[:, None]
-        assert_close(torch.from_numpy(g[mask]), want[mask], what)
+        assert_close(torch.from_numpy(g[mask]), want[mask], what, mag=mag[mask])
     else:
-        gs, ws = [], []
+        gs, ws, ms = [], [], []
         for b, h in pairs:
             n = lens_a[b]
-            w = attn.dense_attention(q[b:b + 1, :, h:h + 1].float().numpy(), k[b:b + 1, :, h:h + 1].float().numpy(),
-                                     v[b:b + 1, :, h:h + 1].float().numpy(), [n], causal, 0.125)
+            w, m = attn.dense_attention(q[b:b + 1, :, h:h + 1].float().numpy(),
+                                        k[b:b + 1, :, h:h + 1].float().numpy(),
+                                        v[b:b + 1, :, h:h + 1].float().numpy(), [n], causal, 0.125,
+                                        with_magnitude=True)
             gs.append(g[b, :n, h])
             ws.append(w[0, :n, 0])
-        assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what)
+            ms.append(m[0, :n, 0])
+        assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what, mag=np.concatenate(ms))
 
 
 @pytest.mark.parametrize("causal", [False, True])

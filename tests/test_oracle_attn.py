@@ -178,3 +178,24 @@ def test_split_key_merge_identity(cuts):
     full = attn.decode_attention_dequant(q.reshape(1, 1, 64), kh.reshape(1, 1, L, 64),
                                          vh.reshape(1, 1, L, 64), [L], 0.125)[0, 0]
     np.testing.assert_allclose(merged, full, rtol=1e-12, atol=1e-14)
+
+
+def test_magnitude_is_weighted_abs_v():
+    """The tolerance normaliser: equals O when V >= 0, bounds |O|, and matches
+    a brute-force weighted mean of |V|."""
+    g = np.random.default_rng(7)
+    q, k, v = (g.standard_normal((2, 9, 2, 4)) for _ in range(3))
+    lens = np.array([9, 4])
+    out, mag = attn.dense_attention(q, k, v, lens, True, 0.5, with_magnitude=True)
+    out_abs, mag_abs = attn.dense_attention(q, k, np.abs(v), lens, True, 0.5, with_magnitude=True)
+    fin = ~np.isnan(out)
+    np.testing.assert_allclose(mag_abs[fin], out_abs[fin], rtol=1e-13)
+    np.testing.assert_allclose(mag[fin], mag_abs[fin], rtol=1e-13)
+    assert np.all(mag[fin] >= np.abs(out[fin]) - 1e-13)
+    want = _brute_dense(q, k, np.abs(v), lens, True, 0.5)
+    np.testing.assert_allclose(mag[fin], want[fin], rtol=1e-12)
+    qd = g.standard_normal((2, 2, 4))
+    kh, vh = g.standard_normal((2, 2, 5, 4)), g.standard_normal((2, 2, 5, 4))
+    o2, m2 = attn.decode_attention_dequant(qd, kh, vh, [5, 2], 0.5, with_magnitude=True)
+    o3 = attn.decode_attention_dequant(qd, kh, np.abs(vh), [5, 2], 0.5)
+    np.testing.assert_allclose(m2, o3, rtol=1e-13)

@@ -4,8 +4,9 @@
 // whisper-blaze 0.1.8 ("Direct Kernel API"), placed in the model as in
 // "Unlocking the power of OpenAI's Whisper", section 3.
 //
-// One block = 4 waves = 128 queries of one (b, h); each wave owns 32 queries
-// and walks the keys in tiles of 64 staged through LDS (double buffered).
+// One block = 4 waves = 256 queries of one (b, h); each wave owns 64 queries
+// (two 32-query MFMA blocks, so every K and V fragment read from LDS feeds
+// two MFMAs) and walks the keys in tiles of 64.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form, so the
 // accumulator's lane index is the query:
@@ -16,12 +17,22 @@
 // is lane-local.  The K rows fed to the first product are permuted (bits 2
 // and 3 of the row index swapped) so that the S^T accumulator registers come
 // out already in the B-operand order of the second product: P^T is converted
-// to bf16 in place, with no shuffles.  V is transposed once per tile while it
-// is written to LDS; all LDS tiles use an XOR swizzle of their 16-byte
-// chunks so the MFMA operand reads are bank-conflict free.
+// to bf16 in place, with no shuffles.
 //
-// The softmax is online (running max and sum per query) in the exp2 domain:
-// softmax_scale * log2(e) is folded into one FMA per score.
+// K and V tiles are copied global -> LDS by the asynchronous 16-byte
+// global_load_lds instruction (no register staging) into a 2-stage ring: the
+// copy of tile t+1 is issued as soon as tile t's operands are in registers,
+// so it lands while tile t's softmax and P.V run; one barrier per tile.  Both tiles are
+// stored row-major with an XOR swizzle of their 16-byte chunks (the swizzle is
+// applied by choosing which global chunk each lane fetches, since the LDS
+// destination of that instruction is fixed per lane).  The V^T operand is
+// read with gfx950's transposing LDS read ds_read_b64_tr_b16: within each 16
+// lanes it returns 4 keys x 1 dim per lane from 4 rows x 16 dims.
+//
+// Softmax: online, in the exp2 domain (softmax_scale * log2(e) folded into one
+// FMA per score), with a lazy rescale -- the running max moves only when a
+// tile max exceeds it by more than 2^8 -- and row sums taken from the bf16
+// weights with v_dot2_f32_bf16 (two weights per instruction).
 #include <cmath>
 
 #include "wa_internal.h"
@@ -34,10 +45,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;   // queries per block
+constexpr int kQW = 64;            // queries per wave (two 32-query MFMA blocks)
+constexpr int kBM = kWaves * kQW;  // queries per block
 constexpr int kBN = 64;            // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;      // lazy-rescale threshold, log2 units
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // 16-byte chunk swizzle of a 128-byte LDS row
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -51,62 +67,43 @@ __device__ __forceinline__ int swap_bits23(int m) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // v_cvt_pk_bf16_f32: round to nearest even
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-struct TileRegs {
-  uint4 k[2];
-  uint4 v[2];
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+constexpr int kStages = 2;
+// s_waitcnt immediate with vmcnt = 0 and expcnt / lgkmcnt left at their maxima
+constexpr int kVmcnt0 = 0x3F70;
+constexpr int kStageBytes = 2 * kTileBytes;  // K then V
 
-__device__ __forceinline__ void load_tile(TileRegs &t, const uint16_t *kp, wa_strides ks,
-                                          const uint16_t *vp, wa_strides vs, int k0, int kend,
-                                          int tid) {
-  const int lane = tid & 63, w = tid >> 6;
+// Issue the asynchronous copy of one K/V tile (rows k0 .. k0+63) into a
+// stage.  Wave w copies K rows and V rows [16w, 16w+16), 8 rows per
+// instruction; lane l lands in 16-byte LDS slot l of the instruction's 1 KB
+// and fetches the global chunk that the swizzle assigns to that slot.  Rows
+// at or past kend are clamped to row kend-1 (finite data; their scores are
+// masked to -inf, so they carry zero weight).
+__device__ __forceinline__ void issue_tile(uint8_t *stage, const uint16_t *kp, wa_strides ks,
+                                           const uint16_t *vp, wa_strides vs, int k0, int kend,
+                                           int lane, int w) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = tid + i * kThreads;
-    const int row = p >> 3, ch = p & 7;
-    const int j = k0 + row;
-    t.k[i] = j < kend ? *reinterpret_cast<const uint4 *>(kp + (long)j * ks.t + ch * 8)
-                      : make_uint4(0, 0, 0, 0);
-  }
-  const int pair = w * 8 + (lane >> 3), ch = lane & 7;
-  const int j = k0 + 2 * pair;
-  t.v[0] = j < kend ? *reinterpret_cast<const uint4 *>(vp + (long)j * vs.t + ch * 8)
-                    : make_uint4(0, 0, 0, 0);
-  t.v[1] = j + 1 < kend ? *reinterpret_cast<const uint4 *>(vp + (long)(j + 1) * vs.t + ch * 8)
-                        : make_uint4(0, 0, 0, 0);
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs &t, uint8_t *kl, uint8_t *vtl, int tid) {
-  const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + i * kThreads;
-    const int row = p >> 3, ch = p & 7;
-    *reinterpret_cast<uint4 *>(kl + lds_off(row, ch)) = t.k[i];
-  }
-  // V^T: dims become rows; this thread holds keys 2*pair and 2*pair+1
-  const int pair = w * 8 + (lane >> 3), ch = lane & 7;
-  const uint32_t a[4] = {t.v[0].x, t.v[0].y, t.v[0].z, t.v[0].w};
-  const uint32_t b[4] = {t.v[1].x, t.v[1].y, t.v[1].z, t.v[1].w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t word = (i & 1) ? ((a[i >> 1] >> 16) | (b[i >> 1] & 0xffff0000u))
-                                  : ((a[i >> 1] & 0xffffu) | (b[i >> 1] << 16));
-    const int d = ch * 8 + i;
-    *reinterpret_cast<uint32_t *>(vtl + lds_off(d, pair >> 2) + (pair & 3) * 4) = word;
+    const int row = w * 16 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    const int j = min(k0 + row, kend - 1);
+    uint8_t *dst = stage + (w * 16 + i * 8) * 128;
+    __builtin_amdgcn_global_load_lds(kp + (long)j * ks.t + chunk * 8, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + (long)j * vs.t + chunk * 8, dst + kTileBytes, 16, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void encoder_attn_kernel(
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
-    int T_max, const int32_t *__restrict__ lens, int causal, float c_log2, int n_qt, int total) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];
+    int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][kStageBytes];
 
   // XCD-aware order: blocks are dispatched round robin over the 8 XCDs, so
   // block L runs on XCD L % 8.  Give each XCD a contiguous run of work items
@@ -116,139 +113,195 @@ __global__ __launch_bounds__(kThreads, 2) void encoder_attn_kernel(
   if (item >= total) return;
   const int bh = item / n_qt;
   int qt = item - bh * n_qt;
-  if (causal) qt = n_qt - 1 - qt;  // longest rows first
+  if (kCausal) qt = n_qt - 1 - qt;  // longest rows first
   const int b = bh / H, h = bh - b * H;
   const int len = min(max(lens ? lens[b] : T_max, 0), T_max);
   const int q0 = qt * kBM;
   if (q0 >= len) return;
-  const int kend = causal ? min(len, q0 + kBM) : len;
+  const int kend = kCausal ? min(len, q0 + kBM) : len;
   const int nt = (kend + kBN - 1) / kBN;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int my_q = q0 + w * 32 + col;
-
-  // Q^T operand: lane holds query my_q, dims c*16 + half*8 .. +8
-  bf16x8 qreg[4];
-  {
-    const uint16_t *qp = q + (long)b * qs.b + (long)my_q * qs.t + (long)h * qs.h + half * 8;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (my_q < len) {
-        qreg[c] = *reinterpret_cast<const bf16x8 *>(qp + c * 16);
-      } else {
-        qreg[c] = bf16x8{};
-      }
-    }
-  }
+  const int wq_lo = q0 + w * kQW;  // this wave's first query
 
   const uint16_t *kp = k + (long)b * ks.b + (long)h * ks.h;
   const uint16_t *vp = v + (long)b * vs.b + (long)h * vs.h;
+  issue_tile(lds[0], kp, ks, vp, vs, 0, kend, lane, w);
 
-  f32x16 oacc[2];
-  oacc[0] = f32x16{};
-  oacc[1] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // Q^T operands: q-block qb holds query wq_lo + qb*32 + col, dims c*16 + half*8 .. +8
+  bf16x8 qreg[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = wq_lo + qb * 32 + col;
+    const uint16_t *qp = q + (long)b * qs.b + (long)my_q * qs.t + (long)h * qs.h + half * 8;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+  }
 
-  TileRegs pre;
-  load_tile(pre, kp, ks, vp, vs, 0, kend, tid);
-  store_tile(pre, lds[0][0], lds[0][1], tid);
-  __syncthreads();
+  f32x16 oacc[2][2];  // [d block][q block]
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x16{};
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max, exp2 domain
+  float l_run[2] = {0.f, 0.f};              // running sum over this lane's half of the keys
 
-  const int wq_lo = q0 + w * 32;  // this wave's first query
+  // per-lane parts of the transposing V^T read: source row j and dims 4q
+  const int tr_a = lane & 15;
+  const int tr_row = (half * 8) + (tr_a >> 2);          // + c*16 + th*4
+  const int tr_col = ((lane >> 4) & 1) * 16 + (tr_a & 3) * 4;  // + db*32
+
   for (int kt = 0; kt < nt; ++kt) {
     const int k0 = kt * kBN;
-    if (kt + 1 < nt) load_tile(pre, kp, ks, vp, vs, k0 + kBN, kend, tid);
+    // This wave's copies of tile kt are complete (the compiler does not order
+    // the asynchronous LDS copies before the barrier by itself), then the
+    // barrier: tile kt is in LDS and every wave is done with tile kt-1.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    // causal: a wave whose every query precedes every key of the tile skips it
+    const bool skip = kCausal && k0 > wq_lo + kQW - 1;
+    if (skip) {
+      if (kt + 1 < nt) issue_tile(lds[(kt + 1) % kStages], kp, ks, vp, vs, k0 + kBN, kend, lane, w);
+      continue;
+    }
+    const uint8_t *kl = lds[kt % kStages];
+    const uint8_t *vl = kl + kTileBytes;
 
-    const bool skip = causal && k0 > wq_lo + 31;  // every key after every query of this wave
-    if (!skip) {
-      const uint8_t *kl = lds[kt & 1][0];
-      const uint8_t *vtl = lds[kt & 1][1];
-
-      f32x16 s[2];
+    // S^T = K . Q^T: each K fragment feeds both query blocks
+    f32x16 s[2][2];  // [key block][q block]
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int row = kb * 32 + swap_bits23(col);
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = kb * 32 + swap_bits23(col);
+      bf16x8 ka[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kl + lds_off(row, c * 2 + half));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], s[kb], 0, 0, 0);
-        }
+      for (int c = 0; c < 4; ++c)
+        ka[c] = *reinterpret_cast<const bf16x8 *>(kl + lds_off(row, c * 2 + half));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[kb][qb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c], s[kb][qb], 0, 0, 0);
       }
+    }
 
-      // s[kb][r] is the score of query my_q and key k0 + kb*32 + (r/8)*16 + half*8 + r%8
-      const bool need_mask = (k0 + kBN > len) || (causal && k0 + kBN - 1 > wq_lo);
+    // s[kb][qb][r]: query wq_lo + qb*32 + col, key k0 + kb*32 + (r/8)*16 + half*8 + r%8
+    const bool tail = k0 + kBN > len;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool need_mask = tail || (kCausal && k0 + kBN - 1 > wq_lo + qb * 32);
       if (need_mask) {
+        // the key's offset in the tile is a constant per (kb, r): compare it
+        // with this lane's limit instead of forming every key index
+        const int my_q = wq_lo + qb * 32 + col;
+        int lim = len - 1 - k0 - half * 8;
+        if (kCausal) lim = min(lim, my_q - k0 - half * 8);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + (r >> 3) * 16 + half * 8 + (r & 7);
-            const bool ok = key < len && (!causal || key <= my_q);
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            const int off = kb * 32 + (r >> 3) * 16 + (r & 7);
+            s[kb][qb][r] = off <= lim ? s[kb][qb][r] : -INFINITY;
           }
       }
+    }
+    float mt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      mt[qb] = mx * c_log2;
+    }
+    // Lazy rescale: keep the running max unless some query's tile max
+    // exceeds it by more than kLazy (P then stays below 2^kLazy, which the
+    // bf16 weights and fp32 sums carry exactly as well).
+    if (__builtin_amdgcn_ballot_w64(mt[0] > m_run[0] + kLazy || mt[1] > m_run[1] + kLazy) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+        oacc[0][qb] *= alpha;
+        oacc[1][qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+    }
+
+    // V^T operands: lane holds dim db*32 + col and keys c*16 + half*8 .. +8
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s16x4 t[2];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          const int row = c * 16 + th * 4 + tr_row;
+          const int cc = db * 32 + tr_col;
+          t[th] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(vl + lds_off(row, cc >> 3) + (cc & 7) * 2));
+        }
+        va[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    // every LDS operand of tile kt is in registers: start copying tile kt+1
+    // into the other stage (last read in tile kt-1, before the barrier)
+    if (kt + 1 < nt) issue_tile(lds[(kt + 1) % kStages], kp, ks, vp, vs, k0 + kBN, kend, lane, w);
+
+    bf16x8 pb[2][4];  // P^T operands [q block][key chunk]
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mneg = -m_run[qb];
       float lsum = 0.f;
-      bf16x8 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + i], c_log2, -m_new));
-            lsum += p[i];
-          }
           uint32_t wd[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wd[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-          pb[kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
+            wd[i] = pack_bf16x2(p0, p1);
+            // row sum of the bf16 weights actually used by P.V
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[i]), kOnes2, lsum, false);
+          }
+          pb[qb][kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      l_run[qb] += lsum;
+      // O^T += V^T . P^T
 #pragma unroll
-      for (int db = 0; db < 2; ++db) oacc[db] *= alpha;
-
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int d = db * 32 + col;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vtl + lds_off(d, c * 2 + half));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
-        }
-      }
+        for (int c = 0; c < 4; ++c)
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[qb][c], oacc[db][qb], 0, 0, 0);
     }
-
-    if (kt + 1 < nt) store_tile(pre, lds[(kt + 1) & 1][0], lds[(kt + 1) & 1][1], tid);
-    __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (my_q < len) {
-    const float inv = 1.0f / l_tot;
-    uint16_t *op = o + (long)b * os.b + (long)my_q * os.t + (long)h * os.h;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = wq_lo + qb * 32 + col;
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    if (my_q < len) {
+      const float inv = 1.0f / l_tot;
+      uint16_t *op = o + (long)b * os.b + (long)my_q * os.t + (long)h * os.h;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        // accumulator rows 8*r4 + 4*half + 0..3 are dims db*32 + that
-        const int d = db * 32 + 8 * r4 + 4 * half;
-        uint2 val;
-        val.x = pack_bf16x2(oacc[db][r4 * 4 + 0] * inv, oacc[db][r4 * 4 + 1] * inv);
-        val.y = pack_bf16x2(oacc[db][r4 * 4 + 2] * inv, oacc[db][r4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2 *>(op + d) = val;
-      }
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          // accumulator rows 8*r4 + 4*half + 0..3 are dims db*32 + that
+          const int d = db * 32 + 8 * r4 + 4 * half;
+          uint2 val;
+          val.x = pack_bf16x2(oacc[db][qb][r4 * 4 + 0] * inv, oacc[db][qb][r4 * 4 + 1] * inv);
+          val.y = pack_bf16x2(oacc[db][qb][r4 * 4 + 2] * inv, oacc[db][qb][r4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2 *>(op + d) = val;
+        }
+    }
   }
 }
 
@@ -261,9 +314,14 @@ hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, w
   const int n_qt = (T_max + kBM - 1) / kBM;
   const long total = (long)B * H * n_qt;
   const long grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL(encoder_attn_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, q, qs,
-                     k, ks, v, vs, o, os, H, T_max, lens, causal, softmax_scale * kLog2e, n_qt,
-                     (int)total);
+  if (causal)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q,
+                       qs, k, ks, v, vs, o, os, H, T_max, lens, softmax_scale * kLog2e, n_qt,
+                       (int)total);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q,
+                       qs, k, ks, v, vs, o, os, H, T_max, lens, softmax_scale * kLog2e, n_qt,
+                       (int)total);
   return hipGetLastError();
 }
 

@@ -5,21 +5,22 @@
 // to the KV cache that the HF blog "Blazingly fast whisper transcriptions
 // with Inference Endpoints" (section "Inference Stack") stores in one byte.
 //
-// Two HBM-bound passes:
-//   1. kv_amax_kernel: every thread owns one fixed 16-byte piece position of
-//      a row (so one fixed head) and keeps a register max of |bits & 0x7fff|
-//      over the rows it visits -- an exact, order-free integer max that
-//      equals the fp32 abs-max of the bf16 values.  Each block folds its
-//      threads into per-group maxima in LDS and writes them to the workspace.
-//   2. kv_encode_kernel: each block first folds the per-block maxima into
-//      the group scales (block 0 also stores them), then every thread
-//      divides its 8 values by the scale (IEEE fp32 division), clamps to
-//      +-448 and converts with the hardware OCP fp8 conversion
-//      (round-to-nearest-even), writing 8 code bytes to the cache slot.
+// Grid shape shared by the two streaming kernels: block (b, c) covers rows
+// t in [c*kRows, (c+1)*kRows) of sequence b, clipped to lens[b] (one scalar
+// load per block; blocks past the length exit at once).  A row is H*64 bf16,
+// split into H*8 pieces of 16 bytes; thread p of a block owns piece p of
+// every row it visits, so its head -- and its scale group -- never changes.
 //
-// The total thread count of both grids is a multiple of the number of
-// pieces per row, so the piece (and head) of a thread never changes while it
-// strides over rows.
+//   kv_amax_kernel      register max of |bits & 0x7fff| per thread (an exact,
+//                       order-free integer max equal to the fp32 abs-max of
+//                       the bf16 values), folded per group in LDS and stored
+//                       as one partial per block and group.
+//   kv_scale_kernel     one block folds the partials and writes
+//                       scale[g] = amax_g / 448 (1 when amax_g is 0).
+//   kv_encode_kernel    reads scale[g]; each thread divides its 8 values by
+//                       it (IEEE fp32 division), clamps to +-448, converts with
+//                       the hardware OCP fp8 conversion (round to nearest
+//                       even) and writes 8 code bytes into the cache slot.
 #include <algorithm>
 
 #include "wa_internal.h"
@@ -27,11 +28,11 @@
 namespace wa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsUnroll = 4;
+constexpr int kRows = 32;       // rows of one sequence per block
+constexpr int kUnroll = 8;      // loads in flight per thread
 
 __device__ __forceinline__ uint32_t maxabs_bits8(uint4 v) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -43,16 +44,13 @@ __device__ __forceinline__ uint32_t maxabs_bits8(uint4 v) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float clamp448(float y) { return fminf(fmaxf(y, -448.0f), 448.0f); }
 
-__device__ __forceinline__ float clamp448(float y) {
-  return fminf(fmaxf(y, -448.0f), 448.0f);
-}
-
-// 8 bf16 -> 8 E4M3 codes (RNE, saturated by the clamp).  The division is
-// the IEEE correctly rounded fp32 quotient (the library is built without
-// fast-math and with correctly rounded fp32 division).
+// 8 bf16 -> 8 E4M3 codes.  The quotient is the IEEE correctly rounded fp32
+// division (the library is built without fast-math and with correctly
+// rounded fp32 division); the clamp makes the conversion saturate.
 __device__ __forceinline__ uint2 encode8(uint4 v, float s) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -67,112 +65,101 @@ __device__ __forceinline__ uint2 encode8(uint4 v, float s) {
 }
 
 __device__ __forceinline__ int seq_len(const int32_t *lens, int b, int T_max) {
-  int n = lens ? lens[b] : T_max;
+  const int n = lens ? lens[b] : T_max;
   return min(max(n, 0), T_max);
 }
 
-__global__ __launch_bounds__(kThreads) void kv_amax_kernel(
-    const uint16_t *__restrict__ x, wa_strides xs, int B, int T_max, int P,
-    const int32_t *__restrict__ lens, int per_head, int groups, uint32_t *__restrict__ partial) {
+__global__ __launch_bounds__(1024) void kv_amax_kernel(const uint16_t *__restrict__ x,
+                                                       wa_strides xs, int T_max, int P,
+                                                       const int32_t *__restrict__ lens,
+                                                       int per_head, int groups,
+                                                       uint32_t *__restrict__ partial) {
   extern __shared__ uint32_t smax[];  // [groups]
-  for (int g = threadIdx.x; g < groups; g += kThreads) smax[g] = 0;
+  const int b = blockIdx.x;
+  const int t0 = blockIdx.y * kRows;
+  const int t1 = min(t0 + kRows, seq_len(lens, b, T_max));
+  const long blk = (long)blockIdx.y * gridDim.x + blockIdx.x;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) smax[g] = 0;
   __syncthreads();
-
-  const long gtid = (long)blockIdx.x * kThreads + threadIdx.x;
-  const long TT = (long)gridDim.x * kThreads;
-  const int p = (int)(gtid % P);
-  const int h = p >> 3;
-  const int d0 = (p & 7) * 8;
-  const long rstride = TT / P;  // exact: TT is a multiple of P
-  const long nrows = (long)B * T_max;
-  const uint16_t *xh = x + (long)h * xs.h + d0;
-
-  uint32_t m = 0;
-  for (long row = gtid / P; row < nrows; row += kRowsUnroll * rstride) {
-    uint4 v[kRowsUnroll];
-    bool ok[kRowsUnroll];
+  if (t0 < t1) {
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+      const uint16_t *xp = x + (long)b * xs.b + (long)(p >> 3) * xs.h + (p & 7) * 8;
+      uint32_t m = 0;
+      for (int t = t0; t < t1; t += kUnroll) {
+        uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u) {
-      long r = row + u * rstride;
-      int b = (int)(r / T_max);
-      int t = (int)(r - (long)b * T_max);
-      ok[u] = r < nrows && t < seq_len(lens, b, T_max);
-      if (ok[u]) v[u] = *reinterpret_cast<const uint4 *>(xh + (long)b * xs.b + (long)t * xs.t);
+        for (int u = 0; u < kUnroll; ++u)
+          v[u] = t + u < t1 ? *reinterpret_cast<const uint4 *>(xp + (long)(t + u) * xs.t)
+                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) m = max(m, maxabs_bits8(v[u]));
+      }
+      atomicMax(&smax[per_head ? (p >> 3) : 0], m);
     }
-#pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u)
-      if (ok[u]) m = max(m, maxabs_bits8(v[u]));
   }
-  atomicMax(&smax[per_head ? h : 0], m);
   __syncthreads();
-  for (int g = threadIdx.x; g < groups; g += kThreads)
-    partial[(long)blockIdx.x * groups + g] = smax[g];
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) partial[blk * groups + g] = smax[g];
 }
 
-__global__ __launch_bounds__(kThreads) void kv_encode_kernel(
-    const uint16_t *__restrict__ x, wa_strides xs, int B, int T_max, int P,
-    const int32_t *__restrict__ lens, const int32_t *__restrict__ dst_start,
-    uint8_t *__restrict__ cache, wa_strides cs, int cache_len, float *__restrict__ scale,
-    int per_head, int groups, int compute_scale, const uint32_t *__restrict__ partial,
-    int amax_blocks) {
+__global__ __launch_bounds__(1024) void kv_scale_kernel(const uint32_t *__restrict__ partial,
+                                                        int n_blocks, int groups,
+                                                        float *__restrict__ scale) {
   extern __shared__ uint32_t smax[];  // [groups]
-  const long gtid = (long)blockIdx.x * kThreads + threadIdx.x;
-  const long TT = (long)gridDim.x * kThreads;
-  const int p = (int)(gtid % P);
-  const int h = p >> 3;
-  const int d0 = (p & 7) * 8;
-  const int g = per_head ? h : 0;
-
-  float s;
-  if (compute_scale) {
-    for (int i = threadIdx.x; i < groups; i += kThreads) smax[i] = 0;
-    __syncthreads();
-    const long n = (long)amax_blocks * groups;
-    for (long i = threadIdx.x; i < n; i += kThreads) atomicMax(&smax[i % groups], partial[i]);
-    __syncthreads();
-    // amax as fp32 (bf16 bits shifted into place), scale = amax / 448
-    const float amax = __uint_as_float(smax[g] << 16);
-    s = amax == 0.0f ? 1.0f : amax / 448.0f;
-    if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < groups; i += kThreads) {
-        const float a = __uint_as_float(smax[i] << 16);
-        scale[i] = a == 0.0f ? 1.0f : a / 448.0f;
-      }
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) smax[g] = 0;
+  __syncthreads();
+  if (groups <= (int)blockDim.x) {
+    // thread -> one group and a strided subset of the blocks' partials
+    const int per = blockDim.x / groups;
+    if ((int)threadIdx.x < per * groups) {
+      const int g = threadIdx.x % groups;
+      uint32_t m = 0;
+      for (long j = threadIdx.x / groups; j < n_blocks; j += per) m = max(m, partial[j * groups + g]);
+      atomicMax(&smax[g], m);
     }
   } else {
-    s = scale[g];
-  }
-
-  const long rstride = TT / P;
-  const long nrows = (long)B * T_max;
-  const uint16_t *xh = x + (long)h * xs.h + d0;
-  uint8_t *ch = cache + (long)h * cs.h + d0;
-  for (long row = gtid / P; row < nrows; row += kRowsUnroll * rstride) {
-    uint4 v[kRowsUnroll];
-    long dst[kRowsUnroll];
-    bool ok[kRowsUnroll];
-#pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u) {
-      long r = row + u * rstride;
-      int b = (int)(r / T_max);
-      int t = (int)(r - (long)b * T_max);
-      ok[u] = false;
-      if (r < nrows && t < seq_len(lens, b, T_max)) {
-        int slot = (dst_start ? dst_start[b] : 0) + t;
-        if (slot >= 0 && slot < cache_len) {
-          ok[u] = true;
-          dst[u] = (long)b * cs.b + (long)slot * cs.t;
-          v[u] = *reinterpret_cast<const uint4 *>(xh + (long)b * xs.b + (long)t * xs.t);
-        }
-      }
+    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+      uint32_t m = 0;
+      for (long j = 0; j < n_blocks; ++j) m = max(m, partial[j * groups + g]);
+      smax[g] = m;
     }
-#pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u)
-      if (ok[u]) *reinterpret_cast<uint2 *>(ch + dst[u]) = encode8(v[u], s);
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    const float a = __uint_as_float(smax[g] << 16);  // bf16 bits -> fp32, exact
+    scale[g] = a == 0.0f ? 1.0f : a / 448.0f;
   }
 }
 
-int round_to_unit(int want, int unit) { return std::max(unit, (want / unit) * unit); }
+__global__ __launch_bounds__(1024) void kv_encode_kernel(
+    const uint16_t *__restrict__ x, wa_strides xs, int T_max, int P,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ dst_start,
+    uint8_t *__restrict__ cache, wa_strides cs, int cache_len, const float *__restrict__ scale,
+    int per_head) {
+  const int b = blockIdx.x;
+  const int t0 = blockIdx.y * kRows;
+  const int t1 = min(t0 + kRows, seq_len(lens, b, T_max));
+  if (t0 >= t1) return;
+  const int d0 = dst_start ? dst_start[b] : 0;
+  // slots outside [0, cache_len) are skipped
+  const int ta = max(t0, -d0), tb = min(t1, cache_len - d0);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    const int h = p >> 3;
+    const float s = scale[per_head ? h : 0];
+    const uint16_t *xp = x + (long)b * xs.b + (long)h * xs.h + (p & 7) * 8;
+    uint8_t *cp = cache + (long)b * cs.b + (long)h * cs.h + (long)d0 * cs.t + (p & 7) * 8;
+    for (int t = ta; t < tb; t += kUnroll) {
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (t + u < tb) v[u] = *reinterpret_cast<const uint4 *>(xp + (long)(t + u) * xs.t);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (t + u < tb) *reinterpret_cast<uint2 *>(cp + (long)(t + u) * cs.t) = encode8(v[u], s);
+    }
+  }
+}
+
+int block_threads(int P) { return std::min(1024, ((P + 63) / 64) * 64); }
 
 }  // namespace
 
@@ -180,22 +167,14 @@ QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran) {
   QuantPlan p;
   p.pieces_per_row = H * 8;
   p.groups = gran == WA_SCALE_PER_HEAD ? H : 1;
-  // block counts whose thread totals are multiples of pieces_per_row
-  const int P = p.pieces_per_row;
-  int g = std::__gcd(kThreads, P);
-  int unit = P / g;
-  long rows = (long)B * T_max;
-  long want_threads = std::max<long>(P, std::min<long>(rows * P, 512L * kThreads));
-  int want_blocks = (int)((want_threads + kThreads - 1) / kThreads);
-  p.amax_blocks = round_to_unit(std::min(want_blocks, 512), unit);
-  long enc_threads = std::max<long>(P, std::min<long>(rows * P, 2048L * kThreads));
-  int enc_blocks = (int)((enc_threads + kThreads - 1) / kThreads);
-  p.encode_blocks = round_to_unit(std::min(enc_blocks, 2048), unit);
+  p.row_chunks = (T_max + kRows - 1) / kRows;
+  p.blocks = (long)B * p.row_chunks;
+  p.threads = block_threads(p.pieces_per_row);
   return p;
 }
 
 size_t quant_workspace_bytes(const QuantPlan &p) {
-  size_t n = (size_t)p.amax_blocks * p.groups * sizeof(uint32_t);
+  const size_t n = (size_t)p.blocks * p.groups * sizeof(uint32_t);
   return (n + 255) & ~(size_t)255;
 }
 
@@ -205,16 +184,20 @@ hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T
                            int compute_scale, uint32_t *ws, const QuantPlan &plan,
                            hipStream_t stream) {
   (void)H;
+  const dim3 grid(B, plan.row_chunks);
   const size_t lds = (size_t)plan.groups * sizeof(uint32_t);
   if (compute_scale) {
-    hipLaunchKernelGGL(kv_amax_kernel, dim3(plan.amax_blocks), dim3(kThreads), lds, stream, x,
-                       xs, B, T_max, plan.pieces_per_row, lens, per_head, plan.groups, ws);
+    hipLaunchKernelGGL(kv_amax_kernel, grid, dim3(plan.threads), lds, stream, x, xs, T_max,
+                       plan.pieces_per_row, lens, per_head, plan.groups, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kv_scale_kernel, dim3(1), dim3(1024), lds, stream, ws, (int)plan.blocks,
+                       plan.groups, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kv_encode_kernel, dim3(plan.encode_blocks), dim3(kThreads), lds, stream, x,
-                     xs, B, T_max, plan.pieces_per_row, lens, dst_start, cache, cs, cache_len,
-                     scale, per_head, plan.groups, compute_scale, ws, plan.amax_blocks);
+  hipLaunchKernelGGL(kv_encode_kernel, grid, dim3(plan.threads), 0, stream, x, xs, T_max,
+                     plan.pieces_per_row, lens, dst_start, cache, cs, cache_len, scale, per_head);
   return hipGetLastError();
 }
 

@@ -14,8 +14,9 @@ namespace wa {
 struct QuantPlan {
   int pieces_per_row;   // H * 8: one piece = 8 bf16 = 16 bytes
   int groups;           // 1 (per tensor) or H (per head)
-  int amax_blocks;      // blocks of the abs-max pass
-  int encode_blocks;    // blocks of the encode pass
+  int row_chunks;       // blocks per sequence (rows of one block: a fixed chunk)
+  long blocks;          // B * row_chunks
+  int threads;          // threads per block (pieces_per_row rounded up to waves)
 };
 QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran);
 size_t quant_workspace_bytes(const QuantPlan &p);
