@@ -20,9 +20,9 @@
 // to bf16 in place, with no shuffles.
 //
 // K and V tiles are copied global -> LDS by the asynchronous 16-byte
-// global_load_lds instruction (no register staging) into a 2-stage ring: the
-// copy of tile t+1 is issued as soon as tile t's operands are in registers,
-// so it lands while tile t's softmax and P.V run; one barrier per tile.  Both tiles are
+// global_load_lds instruction (no register staging) into two stages: the copy
+// of tile t+1 is issued right after the barrier that opens tile t, so it lands
+// while tile t is computed; one barrier per tile.  Both tiles are
 // stored row-major with an XOR swizzle of their 16-byte chunks (the swizzle is
 // applied by choosing which global chunk each lane fetches, since the LDS
 // destination of that instruction is fixed per lane).  The V^T operand is
@@ -98,13 +98,152 @@ __device__ __forceinline__ void issue_tile(uint8_t *stage, const uint16_t *kp, w
   }
 }
 
+__device__ __forceinline__ float max_with_lane_xor32(float x) {
+  // v_permlane32_swap: each lane gets its own value and that of lane ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// Per-wave state of the online softmax.
+struct WaveState {
+  bf16x8 qreg[2][4];   // Q^T operands [q block][dim chunk]
+  f32x16 oacc[2][2];   // O^T accumulators [d block][q block]
+  float m_run[2];      // running max per query, exp2 domain
+  float l_run[2];      // running sum over this lane's half of the keys
+};
+
+// One 64-key tile of one wave: S^T = K.Q^T, masked online softmax, O^T += V^T.P^T.
+template <bool kCausal>
+__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t *kl, int k0, int len,
+                                            int wq_lo, float c_log2, int lane) {
+  const int half = lane >> 5, col = lane & 31;
+  const uint8_t *vl = kl + kTileBytes;
+
+  // S^T = K . Q^T: each K fragment feeds both query blocks
+  f32x16 s[2][2];  // [key block][q block]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = kb * 32 + swap_bits23(col);
+    bf16x8 ka[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      ka[c] = *reinterpret_cast<const bf16x8 *>(kl + lds_off(row, c * 2 + half));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[kb][qb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], st.qreg[qb][c], s[kb][qb], 0, 0, 0);
+    }
+  }
+
+  // s[kb][qb][r]: query wq_lo + qb*32 + col, key k0 + kb*32 + (r/8)*16 + half*8 + r%8
+  const bool tail = k0 + kBN > len;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const bool need_mask = tail || (kCausal && k0 + kBN - 1 > wq_lo + qb * 32);
+    if (need_mask) {
+      // the key's offset in the tile is a constant per (kb, r): compare it
+      // with this lane's limit instead of forming every key index
+      const int my_q = wq_lo + qb * 32 + col;
+      int lim = len - 1 - k0 - half * 8;
+      if (kCausal) lim = min(lim, my_q - k0 - half * 8);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + (r >> 3) * 16 + (r & 7);
+          s[kb][qb][r] = off <= lim ? s[kb][qb][r] : -INFINITY;
+        }
+    }
+  }
+  float mt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+    mt[qb] = max_with_lane_xor32(mx) * c_log2;
+  }
+  // Lazy rescale: keep the running max unless some query's tile max exceeds
+  // it by more than kLazy (P then stays below 2^kLazy, which the bf16
+  // weights and fp32 sums carry exactly as well).
+  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m_run[0] + kLazy || mt[1] > st.m_run[1] + kLazy) != 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_new = fmaxf(st.m_run[qb], mt[qb]);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+      st.l_run[qb] *= alpha;
+      st.oacc[0][qb] *= alpha;
+      st.oacc[1][qb] *= alpha;
+      st.m_run[qb] = m_new;
+    }
+  }
+
+  // V^T operands: lane holds dim db*32 + col and keys c*16 + half*8 .. +8,
+  // gathered by the transposing read from 4 key rows x 16 dims per 16 lanes
+  const int tr_a = lane & 15;
+  const int tr_row = half * 8 + (tr_a >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + (tr_a & 3) * 4;
+  bf16x8 va[2][4];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s16x4 t[2];
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const int row = c * 16 + th * 4 + tr_row;
+        const int cc = db * 32 + tr_col;
+        t[th] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(vl + lds_off(row, cc >> 3) + (cc & 7) * 2));
+      }
+      va[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mneg = -st.m_run[qb];
+    float lsum = 0.f;
+    bf16x8 pb[4];  // P^T operands per key chunk
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
+          wd[i] = pack_bf16x2(p0, p1);
+          // row sum of the bf16 weights actually used by P.V
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[i]), kOnes2, lsum, false);
+        }
+        pb[kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+      }
+    st.l_run[qb] += lsum;
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st.oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], st.oacc[db][qb], 0, 0, 0);
+  }
+}
+
+// Two LDS stages as separate objects: with the loop unrolled by two, every
+// access names its stage statically, so the compiler can see that a copy into
+// one stage does not touch the other and inserts no wait before reading it.
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
+
 template <bool kCausal>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][kStageBytes];
-
   // XCD-aware order: blocks are dispatched round robin over the 8 XCDs, so
   // block L runs on XCD L % 8.  Give each XCD a contiguous run of work items
   // so the query tiles of one (b, h) share that XCD's L2 copy of K and V.
@@ -127,166 +266,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
   const uint16_t *kp = k + (long)b * ks.b + (long)h * ks.h;
   const uint16_t *vp = v + (long)b * vs.b + (long)h * vs.h;
-  issue_tile(lds[0], kp, ks, vp, vs, 0, kend, lane, w);
+  issue_tile(g_stage0, kp, ks, vp, vs, 0, kend, lane, w);
 
-  // Q^T operands: q-block qb holds query wq_lo + qb*32 + col, dims c*16 + half*8 .. +8
-  bf16x8 qreg[2][4];
+  WaveState st;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int my_q = wq_lo + qb * 32 + col;
     const uint16_t *qp = q + (long)b * qs.b + (long)my_q * qs.t + (long)h * qs.h + half * 8;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+      st.qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+#pragma unroll
+    for (int db = 0; db < 2; ++db) st.oacc[db][qb] = f32x16{};
+    st.m_run[qb] = -INFINITY;
+    st.l_run[qb] = 0.f;
   }
 
-  f32x16 oacc[2][2];  // [d block][q block]
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};  // running max, exp2 domain
-  float l_run[2] = {0.f, 0.f};              // running sum over this lane's half of the keys
-
-  // per-lane parts of the transposing V^T read: source row j and dims 4q
-  const int tr_a = lane & 15;
-  const int tr_row = (half * 8) + (tr_a >> 2);          // + c*16 + th*4
-  const int tr_col = ((lane >> 4) & 1) * 16 + (tr_a & 3) * 4;  // + db*32
-
-  for (int kt = 0; kt < nt; ++kt) {
-    const int k0 = kt * kBN;
-    // This wave's copies of tile kt are complete (the compiler does not order
-    // the asynchronous LDS copies before the barrier by itself), then the
-    // barrier: tile kt is in LDS and every wave is done with tile kt-1.
+  // causal: a wave whose every query precedes every key of a tile skips it
+  for (int kt = 0; kt < nt; kt += 2) {
+    // even tile: stage 0; this wave's copies of it are complete (the
+    // compiler does not order the asynchronous copies before the barrier by
+    // itself), then the barrier: tile kt is in LDS, stage 1 is free
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    // causal: a wave whose every query precedes every key of the tile skips it
-    const bool skip = kCausal && k0 > wq_lo + kQW - 1;
-    if (skip) {
-      if (kt + 1 < nt) issue_tile(lds[(kt + 1) % kStages], kp, ks, vp, vs, k0 + kBN, kend, lane, w);
-      continue;
-    }
-    const uint8_t *kl = lds[kt % kStages];
-    const uint8_t *vl = kl + kTileBytes;
-
-    // S^T = K . Q^T: each K fragment feeds both query blocks
-    f32x16 s[2][2];  // [key block][q block]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = kb * 32 + swap_bits23(col);
-      bf16x8 ka[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        ka[c] = *reinterpret_cast<const bf16x8 *>(kl + lds_off(row, c * 2 + half));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[kb][qb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qreg[qb][c], s[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // s[kb][qb][r]: query wq_lo + qb*32 + col, key k0 + kb*32 + (r/8)*16 + half*8 + r%8
-    const bool tail = k0 + kBN > len;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const bool need_mask = tail || (kCausal && k0 + kBN - 1 > wq_lo + qb * 32);
-      if (need_mask) {
-        // the key's offset in the tile is a constant per (kb, r): compare it
-        // with this lane's limit instead of forming every key index
-        const int my_q = wq_lo + qb * 32 + col;
-        int lim = len - 1 - k0 - half * 8;
-        if (kCausal) lim = min(lim, my_q - k0 - half * 8);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + (r >> 3) * 16 + (r & 7);
-            s[kb][qb][r] = off <= lim ? s[kb][qb][r] : -INFINITY;
-          }
-      }
-    }
-    float mt[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mt[qb] = mx * c_log2;
-    }
-    // Lazy rescale: keep the running max unless some query's tile max
-    // exceeds it by more than kLazy (P then stays below 2^kLazy, which the
-    // bf16 weights and fp32 sums carry exactly as well).
-    if (__builtin_amdgcn_ballot_w64(mt[0] > m_run[0] + kLazy || mt[1] > m_run[1] + kLazy) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-        oacc[0][qb] *= alpha;
-        oacc[1][qb] *= alpha;
-        m_run[qb] = m_new;
-      }
-    }
-
-    // V^T operands: lane holds dim db*32 + col and keys c*16 + half*8 .. +8
-    bf16x8 va[2][4];
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s16x4 t[2];
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-          const int row = c * 16 + th * 4 + tr_row;
-          const int cc = db * 32 + tr_col;
-          t[th] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(vl + lds_off(row, cc >> 3) + (cc & 7) * 2));
-        }
-        va[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    // every LDS operand of tile kt is in registers: start copying tile kt+1
-    // into the other stage (last read in tile kt-1, before the barrier)
-    if (kt + 1 < nt) issue_tile(lds[(kt + 1) % kStages], kp, ks, vp, vs, k0 + kBN, kend, lane, w);
-
-    bf16x8 pb[2][4];  // P^T operands [q block][key chunk]
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mneg = -m_run[qb];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
-            wd[i] = pack_bf16x2(p0, p1);
-            // row sum of the bf16 weights actually used by P.V
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[i]), kOnes2, lsum, false);
-          }
-          pb[qb][kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-        }
-      l_run[qb] += lsum;
-      // O^T += V^T . P^T
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[qb][c], oacc[db][qb], 0, 0, 0);
-    }
+    if (kt + 1 < nt) issue_tile(g_stage1, kp, ks, vp, vs, (kt + 1) * kBN, kend, lane, w);
+    if (!(kCausal && kt * kBN > wq_lo + kQW - 1))
+      attend_tile<kCausal>(st, g_stage0, kt * kBN, len, wq_lo, c_log2, lane);
+    if (kt + 1 >= nt) break;
+    // odd tile: stage 1
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    if (kt + 2 < nt) issue_tile(g_stage0, kp, ks, vp, vs, (kt + 2) * kBN, kend, lane, w);
+    if (!(kCausal && (kt + 1) * kBN > wq_lo + kQW - 1))
+      attend_tile<kCausal>(st, g_stage1, (kt + 1) * kBN, len, wq_lo, c_log2, lane);
   }
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int my_q = wq_lo + qb * 32 + col;
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32, 64);
     if (my_q < len) {
       const float inv = 1.0f / l_tot;
       uint16_t *op = o + (long)b * os.b + (long)my_q * os.t + (long)h * os.h;
@@ -297,8 +315,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
           // accumulator rows 8*r4 + 4*half + 0..3 are dims db*32 + that
           const int d = db * 32 + 8 * r4 + 4 * half;
           uint2 val;
-          val.x = pack_bf16x2(oacc[db][qb][r4 * 4 + 0] * inv, oacc[db][qb][r4 * 4 + 1] * inv);
-          val.y = pack_bf16x2(oacc[db][qb][r4 * 4 + 2] * inv, oacc[db][qb][r4 * 4 + 3] * inv);
+          val.x = pack_bf16x2(st.oacc[db][qb][r4 * 4 + 0] * inv, st.oacc[db][qb][r4 * 4 + 1] * inv);
+          val.y = pack_bf16x2(st.oacc[db][qb][r4 * 4 + 2] * inv, st.oacc[db][qb][r4 * 4 + 3] * inv);
           *reinterpret_cast<uint2 *>(op + d) = val;
         }
     }
