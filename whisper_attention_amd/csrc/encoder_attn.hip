@@ -4,7 +4,7 @@
 // whisper-blaze 0.1.8 ("Direct Kernel API"), placed in the model as in
 // "Unlocking the power of OpenAI's Whisper", section 3.
 //
-// One block = 4 waves = 256 queries of one (b, h); each wave owns 64 queries
+// One block = 8 waves = 512 queries of one (b, h); each wave owns 64 queries
 // (two 32-query MFMA blocks, so every K and V fragment read from LDS feeds
 // two MFMAs) and walks the keys in tiles of 64.
 //
@@ -19,20 +19,31 @@
 // out already in the B-operand order of the second product: P^T is converted
 // to bf16 in place, with no shuffles.
 //
+// Ping-pong between two wave groups.  The 8 waves form two groups of four,
+// one wave of each on every SIMD.  Between two barriers (one "interval" per
+// key tile t) group A runs its matrix work first -- P(t-1).V(t-1) and
+// S(t) = K(t).Q^T -- and then the softmax of S(t) on the vector ALU, while
+// group B does the same work in the other order: the softmax of the S(t-1)
+// it carried over the barrier, then P(t-1).V(t-1) and S(t).  So on each SIMD
+// one wave keeps the matrix cores busy while the other runs exp / convert /
+// sum on the vector ALU, and the barrier keeps the two in that phase.
+//
 // K and V tiles are copied global -> LDS by the asynchronous 16-byte
-// global_load_lds instruction (no register staging) into two stages: the copy
-// of tile t+1 is issued right after the barrier that opens tile t, so it lands
-// while tile t is computed; one barrier per tile.  Both tiles are
-// stored row-major with an XOR swizzle of their 16-byte chunks (the swizzle is
-// applied by choosing which global chunk each lane fetches, since the LDS
-// destination of that instruction is fixed per lane).  The V^T operand is
+// global_load_lds instruction (no register staging) into four stages:
+// interval t reads K of tile t and V of tile t-1 and starts the copy of tile
+// t+2, so every copy has two intervals to land; completion is waited for
+// explicitly (vmcnt) before the barrier that publishes a tile.  The interval
+// loop is unrolled by four so every LDS read names its stage with a constant
+// offset.  Tiles are stored row-major with an XOR swizzle of their 16-byte
+// chunks (applied by choosing which global chunk each lane fetches, since the
+// LDS destination of that instruction is fixed per lane).  The V^T operand is
 // read with gfx950's transposing LDS read ds_read_b64_tr_b16: within each 16
 // lanes it returns 4 keys x 1 dim per lane from 4 rows x 16 dims.
 //
 // Softmax: online, in the exp2 domain (softmax_scale * log2(e) folded into one
 // FMA per score), with a lazy rescale -- the running max moves only when a
-// tile max exceeds it by more than 2^8 -- and row sums taken from the bf16
-// weights with v_dot2_f32_bf16 (two weights per instruction).
+// tile max exceeds it by more than 2^8 -- and row sums of the bf16 weights
+// taken on the matrix pipe by a small 16x16x32 MFMA per key chunk.
 #include <cmath>
 
 #include "wa_internal.h"
@@ -41,22 +52,35 @@ namespace wa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kQW = 64;            // queries per wave (two 32-query MFMA blocks)
-constexpr int kBM = kWaves * kQW;  // queries per block
-constexpr int kBN = 64;            // keys per tile
-constexpr int kTileBytes = kBN * 64 * 2;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;      // lazy-rescale threshold, log2 units
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16-byte chunk swizzle of a 128-byte LDS row
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+constexpr int kWaves = 8;                 // two groups of four
+constexpr int kThreads = kWaves * 64;
+constexpr int kQW = 64;                   // queries per wave (two 32-query MFMA blocks)
+constexpr int kBM = kWaves * kQW;         // queries per block
+constexpr int kBN = 64;                   // keys per tile
+constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
+constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;             // lazy-rescale threshold, log2 units
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8): wait until at most N vector-memory operations of
+// this wave are outstanding and all its LDS operations are complete.
+constexpr int kVmcnt0Lgkm0 = 0x0070;
+constexpr int kVmcnt2Lgkm0 = 0x0072;
+
+// 16-byte chunk swizzle of a 128-byte LDS row: the chunk index is XORed with
+// bits 1, 2, 3 of the row, reversed.  The K operand reads (16 rows, one chunk)
+// and the transposing V reads (rows r..r+3 and r+8..r+11, four chunks) then
+// hit distinct banks, and rows 16 apart share a swizzle, so stepping by 16 or
+// 32 rows is a constant offset.
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * 128 + ((chunk ^ swz(row)) << 4);
 }
@@ -64,70 +88,117 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // v_cvt_pk_bf16_f32: round to nearest even
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-constexpr int kStages = 2;
-// s_waitcnt immediate with vmcnt = 0 and expcnt / lgkmcnt left at their maxima
-constexpr int kVmcnt0 = 0x3F70;
-constexpr int kStageBytes = 2 * kTileBytes;  // K then V
-
-// Issue the asynchronous copy of one K/V tile (rows k0 .. k0+63) into a
-// stage.  Wave w copies K rows and V rows [16w, 16w+16), 8 rows per
-// instruction; lane l lands in 16-byte LDS slot l of the instruction's 1 KB
-// and fetches the global chunk that the swizzle assigns to that slot.  Rows
-// at or past kend are clamped to row kend-1 (finite data; their scores are
-// masked to -inf, so they carry zero weight).
-__device__ __forceinline__ void issue_tile(uint8_t *stage, const uint16_t *kp, wa_strides ks,
-                                           const uint16_t *vp, wa_strides vs, int k0, int kend,
-                                           int lane, int w) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = w * 16 + i * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    const int j = min(k0 + row, kend - 1);
-    uint8_t *dst = stage + (w * 16 + i * 8) * 128;
-    __builtin_amdgcn_global_load_lds(kp + (long)j * ks.t + chunk * 8, dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + (long)j * vs.t + chunk * 8, dst + kTileBytes, 16, 0, 0);
-  }
-}
-
 __device__ __forceinline__ float max_with_lane_xor32(float x) {
   // v_permlane32_swap: each lane gets its own value and that of lane ^ 32
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 
+// Per-lane byte offsets of the K (and V) row this lane copies in every
+// tile, relative to the tile's first row: wave w copies rows [8w, 8w+8);
+// lane l lands in 16-byte LDS slot l of the instruction's 1 KB and fetches
+// the global chunk the swizzle assigns to that slot.  Rows at or past kend
+// are clamped to row kend-1 (finite data; their scores are masked to -inf, so
+// they carry zero weight).
+struct CopyOffsets {
+  uint32_t k, v;
+};
+
+__device__ __forceinline__ CopyOffsets copy_offsets(wa_strides ks, wa_strides vs, int max_row,
+                                                    int lane, int w) {
+  const int row = w * 8 + (lane >> 3);
+  const int chunk = (lane & 7) ^ swz(row);
+  const int r = min(row, max_row);
+  return CopyOffsets{(uint32_t)((r * ks.t + chunk * 8) * 2), (uint32_t)((r * vs.t + chunk * 8) * 2)};
+}
+
+// The LDS ring: four stages of one K tile and one V tile each.
+__shared__ __attribute__((aligned(1024))) uint8_t g_lds[4][kStageBytes];
+
+// One asynchronous 16-byte-per-lane copy global -> LDS: lane l's 16 bytes,
+// read from base + voff, land at LDS byte address lds + 16*l.  Written out
+// (rather than with the compiler's global_load_lds builtin) because the
+// compiler cannot tell the stages apart across the interval's branches and
+// would wait for every copy in flight -- including the one two tiles ahead --
+// before each LDS read.  The instruction has no result register; completion
+// is tracked explicitly with s_waitcnt vmcnt before the barrier that
+// publishes a tile.
+__device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// LDS byte address of stage `stage`, as the instruction's M0 wants it.
+__device__ __forceinline__ uint32_t lds_addr(int stage) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_lds[0][0] +
+         stage * kStageBytes;
+}
+
+// Issue the asynchronous copy of the K/V tile that starts at row k0 into a
+// stage.  Wave w fills K rows and V rows [8w, 8w+8) of the stage.
+__device__ __forceinline__ void issue_tile(int stage, const uint16_t *kp, wa_strides ks,
+                                           const uint16_t *vp, wa_strides vs, int k0, int kend,
+                                           const CopyOffsets &full, int lane, int w) {
+  // only the last tile can run past kend
+  const CopyOffsets c = k0 + kBN <= kend ? full : copy_offsets(ks, vs, kend - 1 - k0, lane, w);
+  const uint32_t dst = lds_addr(stage) + w * 8 * 128;
+  copy16_to_lds(kp + (long)k0 * ks.t, c.k, dst);
+  copy16_to_lds(vp + (long)k0 * vs.t, c.v, dst + kTileBytes);
+}
+
 // Per-wave state of the online softmax.
 struct WaveState {
   bf16x8 qreg[2][4];   // Q^T operands [q block][dim chunk]
   f32x16 oacc[2][2];   // O^T accumulators [d block][q block]
+  f32x4 lacc[2];       // row sums of P per q block (16x16 MFMA layout, see row_sum_selector)
   float m_run[2];      // running max per query, exp2 domain
-  float l_run[2];      // running sum over this lane's half of the keys
+  bf16x8 sel;          // 0/1 selector A operand of the row-sum MFMA
 };
 
-// One 64-key tile of one wave: S^T = K.Q^T, masked online softmax, O^T += V^T.P^T.
-template <bool kCausal>
-__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t *kl, int k0, int len,
-                                            int wq_lo, float c_log2, int lane) {
-  const int half = lane >> 5, col = lane & 31;
-  const uint8_t *vl = kl + kTileBytes;
+// Per-lane LDS byte offsets of the operand reads (the same in every tile).
+struct ReadOffsets {
+  int k[4];    // K rows for MFMA c (key block 0; key block 1 is +4096)
+  int v[2][2]; // V^T transposing reads for (db, th); key chunk c is +2048*c
+};
 
-  // S^T = K . Q^T: each K fragment feeds both query blocks
-  f32x16 s[2][2];  // [key block][q block]
+__device__ __forceinline__ ReadOffsets read_offsets(int lane) {
+  const int half = lane >> 5, col = lane & 31;
+  ReadOffsets r;
+  const int krow = swap_bits23(col);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.k[c] = lds_off(krow, c * 2 + half);
+  // transposing read: source lane a = lane & 15 points at key row
+  // c*16 + th*4 + half*8 + a/4 and dims db*32 + ((lane>>4)&1)*16 + (a%4)*4
+  const int a = lane & 15;
+  const int row = half * 8 + (a >> 2);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      const int cc = db * 32 + ((lane >> 4) & 1) * 16 + (a & 3) * 4;
+      r.v[db][th] = lds_off(row + th * 4, cc >> 3) + (cc & 7) * 2;
+    }
+  return r;
+}
+
+// S^T = K . Q^T for one key tile: each K fragment feeds both query blocks.
+// s[kb][qb][r] is the score of query (qb*32 + col) and key
+// kb*32 + (r/8)*16 + half*8 + r%8 of the tile.
+__device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
+                                       const ReadOffsets &ro, f32x16 (&s)[2][2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int row = kb * 32 + swap_bits23(col);
     bf16x8 ka[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      ka[c] = *reinterpret_cast<const bf16x8 *>(kl + lds_off(row, c * 2 + half));
+      ka[c] = *reinterpret_cast<const bf16x8 *>(kl + ro.k[c] + kb * 4096);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       s[kb][qb] = f32x16{};
@@ -136,18 +207,23 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t *kl, in
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], st.qreg[qb][c], s[kb][qb], 0, 0, 0);
     }
   }
+}
 
-  // s[kb][qb][r]: query wq_lo + qb*32 + col, key k0 + kb*32 + (r/8)*16 + half*8 + r%8
-  const bool tail = k0 + kBN > len;
+// Online softmax of one tile's scores (vector ALU only): mask, tile max,
+// lazy rescale of O and l, P = exp2(S*c - m) as bf16 P^T operands, row sums.
+template <bool kCausal>
+__device__ __forceinline__ void softmax_tile(WaveState &st, f32x16 (&s)[2][2], int k0, int len,
+                                             int wq_lo, float c_log2, int lane,
+                                             bf16x8 (&pb)[2][4]) {
+  const int half = lane >> 5, col = lane & 31;
+  if (k0 + kBN > len || (kCausal && k0 + kBN - 1 > wq_lo)) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const bool need_mask = tail || (kCausal && k0 + kBN - 1 > wq_lo + qb * 32);
-    if (need_mask) {
+    for (int qb = 0; qb < 2; ++qb) {
       // the key's offset in the tile is a constant per (kb, r): compare it
       // with this lane's limit instead of forming every key index
-      const int my_q = wq_lo + qb * 32 + col;
       int lim = len - 1 - k0 - half * 8;
-      if (kCausal) lim = min(lim, my_q - k0 - half * 8);
+      if (kCausal) lim = min(lim, wq_lo + qb * 32 + col - k0 - half * 8);
+      asm volatile("" : "+v"(lim));  // keep the compares inside this branch
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -175,39 +251,19 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t *kl, in
     for (int qb = 0; qb < 2; ++qb) {
       const float m_new = fmaxf(st.m_run[qb], mt[qb]);
       const float alpha = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
-      st.l_run[qb] *= alpha;
       st.oacc[0][qb] *= alpha;
       st.oacc[1][qb] *= alpha;
+      // row sums: lane n < 16 holds query n in element 0 and query n+16 in
+      // element 1 (see row_sum_selector); the latter's factor is in lane n+16
+      const float alpha_hi = __shfl(alpha, (lane & 15) + 16, 64);
+      st.lacc[qb][0] *= alpha;
+      st.lacc[qb][1] *= alpha_hi;
       st.m_run[qb] = m_new;
     }
   }
-
-  // V^T operands: lane holds dim db*32 + col and keys c*16 + half*8 .. +8,
-  // gathered by the transposing read from 4 key rows x 16 dims per 16 lanes
-  const int tr_a = lane & 15;
-  const int tr_row = half * 8 + (tr_a >> 2);
-  const int tr_col = ((lane >> 4) & 1) * 16 + (tr_a & 3) * 4;
-  bf16x8 va[2][4];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      s16x4 t[2];
-#pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        const int row = c * 16 + th * 4 + tr_row;
-        const int cc = db * 32 + tr_col;
-        t[th] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(vl + lds_off(row, cc >> 3) + (cc & 7) * 2));
-      }
-      va[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float mneg = -st.m_run[qb];
-    float lsum = 0.f;
-    bf16x8 pb[4];  // P^T operands per key chunk
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -218,29 +274,126 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t *kl, in
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
           wd[i] = pack_bf16x2(p0, p1);
-          // row sum of the bf16 weights actually used by P.V
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[i]), kOnes2, lsum, false);
         }
-        pb[kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+        pb[qb][kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
       }
-    st.l_run[qb] += lsum;
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        st.oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], pb[c], st.oacc[db][qb], 0, 0, 0);
   }
 }
 
-// Two LDS stages as separate objects: with the loop unrolled by two, every
-// access names its stage statically, so the compiler can see that a copy into
-// one stage does not touch the other and inserts no wait before reading it.
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
+// Row sums of P on the matrix pipe, in the matrix phase: the 16x16x32 MFMA
+// with B = a P^T operand (lane l: query l%32, 8 keys of half l/32) and A = a
+// 0/1 selector gives D[0][n] = the sum over the chunk's keys for query n and
+// D[1][n] = the same for query n+16 (lane n, elements 0 and 1).  This keeps
+// the sums off the vector ALU, and v_dot2_f32_bf16, which would halve the
+// vector work, does not overlap with MFMA on gfx950: it would stall the other
+// group's matrix phase.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  // A operand of the 16x16x32 MFMA: lane l holds row m = l%16 and 8 values of
+  // k-group g = l/16.  Row 0 sums groups 0 and 2 (query n), row 1 groups 1, 3.
+  const int m = lane & 15, g = lane >> 4;
+  const bool one = (m == 0 && (g & 1) == 0) || (m == 1 && (g & 1) == 1);
+  const __bf16 v = (__bf16)(one ? 1.0f : 0.0f);
+  return bf16x8{v, v, v, v, v, v, v, v};
+}
+
+// O^T += V^T . P^T for one tile.  V^T operands: lane holds dim db*32 + col and
+// keys c*16 + half*8 .. +8, gathered by the transposing read.
+__device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
+                                              const ReadOffsets &ro, const bf16x8 (&pb)[2][4]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.sel, pb[qb][c], st.lacc[qb], 0, 0, 0);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    bf16x8 va[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vl + ro.v[db][0] + c * 2048));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vl + ro.v[db][1] + c * 2048));
+      va[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st.oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], pb[qb][c], st.oacc[db][qb], 0, 0, 0);
+  }
+}
+
+struct Ctx {
+  const uint16_t *kp, *vp;
+  wa_strides ks, vs;
+  CopyOffsets co;
+  ReadOffsets ro;
+  int nt, kend, len, wq_lo, lane, w, group;
+  float c_log2;
+};
+
+// Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+2 is
+// copied into `ahead` (the stage of tile t-2, whose last reads were in
+// interval t-1).  Both groups pass the same barriers, one per interval.
+__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx &x) {
+  // Keep every instruction of the previous interval above the barrier: the
+  // scheduler would otherwise sink matrix instructions (they touch no memory)
+  // past it and break the two groups' phase alignment.
+  __builtin_amdgcn_sched_barrier(0);
+  // This wave's copies of tile t are complete -- only tile t+1's two copies
+  // may still be in flight -- and so are its LDS reads of interval t-1.  Then
+  // a bare barrier (a workgroup fence would wait for tile t+1's copies too):
+  // afterwards tile t is in LDS for everyone and the stage of tile t-2 is free.
+  if (t + 1 < x.nt)
+    __builtin_amdgcn_s_waitcnt(kVmcnt2Lgkm0);
+  else
+    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if (t + 2 < x.nt) issue_tile(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
+}
+
+// causal: a wave whose every query precedes every key of tile j skips it
+template <bool kCausal>
+__device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
+  return j >= 0 && j < x.nt && !(kCausal && j * kBN > x.wq_lo + kQW - 1);
+}
+
+// Group A: P(t-1).V(t-1) and S(t) on the matrix cores, then softmax(t);
+// P(t) is carried to the next interval.
+template <bool kCausal>
+__device__ __forceinline__ void interval_a(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
+                                           const uint8_t *prev, int ahead, int t,
+                                           const Ctx &x) {
+  open_interval(ahead, t, x);
+  if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
+  if (wave_needs<kCausal>(t, x)) {
+    f32x16 s[2][2];
+    scores(st, cur, x.ro, s);
+    __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
+    softmax_tile<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, pa);
+  }
+}
+
+// Group B: softmax(t-1) of the carried S(t-1) first, then P(t-1).V(t-1) and
+// S(t) on the matrix cores; S(t) is carried to the next interval.
+template <bool kCausal>
+__device__ __forceinline__ void interval_b(WaveState &st, f32x16 (&sb)[2][2], const uint8_t *cur,
+                                           const uint8_t *prev, int ahead, int t,
+                                           const Ctx &x) {
+  open_interval(ahead, t, x);
+  if (wave_needs<kCausal>(t - 1, x)) {
+    bf16x8 pb[2][4];
+    softmax_tile<kCausal>(st, sb, (t - 1) * kBN, x.len, x.wq_lo, x.c_log2, x.lane, pb);
+    __builtin_amdgcn_sched_barrier(0);  // vector phase, then matrix phase
+    accumulate_pv(st, prev + kTileBytes, x.ro, pb);
+  }
+  if (wave_needs<kCausal>(t, x)) scores(st, cur, x.ro, sb);
+}
 
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
@@ -257,54 +410,83 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int len = min(max(lens ? lens[b] : T_max, 0), T_max);
   const int q0 = qt * kBM;
   if (q0 >= len) return;
-  const int kend = kCausal ? min(len, q0 + kBM) : len;
-  const int nt = (kend + kBN - 1) / kBN;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int wq_lo = q0 + w * kQW;  // this wave's first query
-
-  const uint16_t *kp = k + (long)b * ks.b + (long)h * ks.h;
-  const uint16_t *vp = v + (long)b * vs.b + (long)h * vs.h;
-  issue_tile(g_stage0, kp, ks, vp, vs, 0, kend, lane, w);
+  const int group = w >> 2;
+  Ctx x;
+  x.kp = k + (long)b * ks.b + (long)h * ks.h;
+  x.vp = v + (long)b * vs.b + (long)h * vs.h;
+  x.ks = ks;
+  x.vs = vs;
+  x.kend = kCausal ? min(len, q0 + kBM) : len;
+  x.nt = (x.kend + kBN - 1) / kBN;
+  x.len = len;
+  // group A holds queries [q0, q0+256), group B [q0+256, q0+512)
+  x.wq_lo = q0 + group * 4 * kQW + (w & 3) * kQW;
+  x.lane = lane;
+  x.w = w;
+  x.group = group;
+  x.c_log2 = c_log2;
+  x.co = copy_offsets(ks, vs, kBN - 1, lane, w);
+  issue_tile(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
+  if (x.nt > 1) issue_tile(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
+  x.ro = read_offsets(lane);
 
   WaveState st;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int my_q = wq_lo + qb * 32 + col;
+    const int my_q = x.wq_lo + qb * 32 + col;
     const uint16_t *qp = q + (long)b * qs.b + (long)my_q * qs.t + (long)h * qs.h + half * 8;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       st.qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
 #pragma unroll
     for (int db = 0; db < 2; ++db) st.oacc[db][qb] = f32x16{};
+    st.lacc[qb] = f32x4{};
     st.m_run[qb] = -INFINITY;
-    st.l_run[qb] = 0.f;
   }
+  st.sel = row_sum_selector(lane);
+  // Consume the Q loads here, once: otherwise the loop-header merge leaves
+  // them "in flight" for the compiler, which then waits for every outstanding
+  // copy (vmcnt(0)) before the first Q use of each unrolled iteration.
+  asm volatile("" ::"v"(st.qreg[0][0]), "v"(st.qreg[0][1]), "v"(st.qreg[0][2]), "v"(st.qreg[0][3]),
+               "v"(st.qreg[1][0]), "v"(st.qreg[1][1]), "v"(st.qreg[1][2]), "v"(st.qreg[1][3]));
 
-  // causal: a wave whose every query precedes every key of a tile skips it
-  for (int kt = 0; kt < nt; kt += 2) {
-    // even tile: stage 0; this wave's copies of it are complete (the
-    // compiler does not order the asynchronous copies before the barrier by
-    // itself), then the barrier: tile kt is in LDS, stage 1 is free
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    if (kt + 1 < nt) issue_tile(g_stage1, kp, ks, vp, vs, (kt + 1) * kBN, kend, lane, w);
-    if (!(kCausal && kt * kBN > wq_lo + kQW - 1))
-      attend_tile<kCausal>(st, g_stage0, kt * kBN, len, wq_lo, c_log2, lane);
-    if (kt + 1 >= nt) break;
-    // odd tile: stage 1
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    if (kt + 2 < nt) issue_tile(g_stage0, kp, ks, vp, vs, (kt + 2) * kBN, kend, lane, w);
-    if (!(kCausal && (kt + 1) * kBN > wq_lo + kQW - 1))
-      attend_tile<kCausal>(st, g_stage1, (kt + 1) * kBN, len, wq_lo, c_log2, lane);
+  // intervals t = 0 .. nt: tile t's K and tile t-1's V; the stage of tile j
+  // is j % 4.  Each group runs its own loop (its carried operands stay in
+  // registers); both pass one barrier per interval.
+  if (group == 0) {
+    bf16x8 pa[2][4];
+    for (int t = 0; t <= x.nt; t += 4) {
+      interval_a<kCausal>(st, pa, g_lds[0], g_lds[3], 2, t, x);
+      if (t + 1 > x.nt) break;
+      interval_a<kCausal>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
+      if (t + 2 > x.nt) break;
+      interval_a<kCausal>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
+      if (t + 3 > x.nt) break;
+      interval_a<kCausal>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
+    }
+  } else {
+    f32x16 sb[2][2];
+    for (int t = 0; t <= x.nt; t += 4) {
+      interval_b<kCausal>(st, sb, g_lds[0], g_lds[3], 2, t, x);
+      if (t + 1 > x.nt) break;
+      interval_b<kCausal>(st, sb, g_lds[1], g_lds[0], 3, t + 1, x);
+      if (t + 2 > x.nt) break;
+      interval_b<kCausal>(st, sb, g_lds[2], g_lds[1], 0, t + 2, x);
+      if (t + 3 > x.nt) break;
+      interval_b<kCausal>(st, sb, g_lds[3], g_lds[2], 1, t + 3, x);
+    }
   }
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int my_q = wq_lo + qb * 32 + col;
-    const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32, 64);
+    const int my_q = x.wq_lo + qb * 32 + col;
+    // row sum of query col: element 0 (col < 16) or 1 (col >= 16) of lane col%16
+    const float l0 = __shfl(st.lacc[qb][0], col & 15, 64);
+    const float l1 = __shfl(st.lacc[qb][1], col & 15, 64);
+    const float l_tot = col < 16 ? l0 : l1;
     if (my_q < len) {
       const float inv = 1.0f / l_tot;
       uint16_t *op = o + (long)b * os.b + (long)my_q * os.t + (long)h * os.h;
