@@ -82,7 +82,8 @@ def test_long_audio_batch_full_size_sampled(gpu):
     _close(got, _oracle(q, kc, vc, ks, vs, lens_s, "head"), "decode long self (all rows)")
 
 
-@pytest.mark.parametrize("B,H,L", [(1, 1, 77), (3, 2, 1), (2, 3, 300), (5, 4, 1500), (300, 8, 65)])
+@pytest.mark.parametrize("B,H,L", [(1, 1, 77), (3, 2, 1), (2, 3, 300), (5, 4, 1500), (300, 8, 65),
+                                   (32, 20, 600)])
 def test_ragged_edges(gpu, B, H, L):
     import whisper_attention_amd as wa
     announce(f"decode ragged edges B={B} H={H} L={L}")

@@ -62,7 +62,14 @@ def _assert_same(got, want, what):
                           f"{gc[tuple(bad[0])]:#x} vs {wc[tuple(bad[0])]:#x}"
 
 
-@pytest.mark.parametrize("s", [1.0, 0.125, 4.25 / 448, 93.0 / 448, 2.0 ** -20 / 3, 3.0e35])
+# 1/448 .. 93/448: the scales of N(0,1) data with and without x20 outliers;
+# 2^-80 and 2^80 (and the float32 next to each, on the other side) bracket
+# the range where the encoder takes the reciprocal path; 3e35 is the scale of
+# the full bf16 range.
+@pytest.mark.parametrize("s", [1.0, 0.125, 1.0 / 448, 4.25 / 448, 93.0 / 448, 2.0 ** -20 / 3,
+                               2.0 ** -80, float(np.nextafter(np.float32(2.0 ** -80), np.float32(0))),
+                               2.0 ** 80, float(np.nextafter(np.float32(2.0 ** 80), np.float32(np.inf))),
+                               3.0e35])
 def test_exhaustive_bf16_static_scale(gpu, s):
     import whisper_attention_amd as wa
     announce(f"quant exhaustive bf16, static scale {s}")
@@ -79,6 +86,16 @@ def test_exhaustive_bf16_dynamic_scale(gpu):
     for gran in ("tensor", "head"):
         _assert_same(_run_quant(wa, x, None, None, 255, gran), _oracle(x, None, None, 255, gran),
                      f"exhaustive dynamic {gran}")
+    # every bf16 of magnitude <= 16, whose dynamic scale 16/448 is an
+    # ordinary one
+    f = _all_finite_bf16()
+    f = f[np.abs(f) <= 16.0]
+    f = np.concatenate([f, np.zeros((-f.size) % 256, np.float32)])
+    x = torch.from_numpy(f.reshape(1, -1, 4, 64)).to(torch.bfloat16)
+    T = x.shape[1]
+    for gran in ("tensor", "head"):
+        _assert_same(_run_quant(wa, x, None, None, T, gran), _oracle(x, None, None, T, gran),
+                     f"exhaustive |x|<=16 dynamic {gran}")
 
 
 @pytest.mark.parametrize("which", ["self", "cross"])
@@ -160,3 +177,18 @@ def test_deterministic(gpu):
     a = _run_quant(wa, x, [100, 3, 50, 99, 1, 100, 64, 2], None, 100, "head")
     b = _run_quant(wa, x, [100, 3, 50, 99, 1, 100, 64, 2], None, 100, "head")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("H", [1, 3, 17, 160])
+def test_head_counts_and_block_shapes(gpu, H):
+    """Row widths that give each block shape: lcm(64, 8H) threads (H=1, 3),
+    8H rounded up to whole waves (H=17) and threads looping over pieces
+    (H=160, rows wider than 1024 pieces)."""
+    import whisper_attention_amd as wa
+    B, T = 3, 37
+    announce(f"quant head count H={H} B={B} T={T}")
+    x = workloads.bf16_normal((B, T, H, 64), 9, 82, 0.02, 20.0)
+    lens = [37, 1, 20]
+    for gran in ("tensor", "head"):
+        _assert_same(_run_quant(wa, x, lens, None, T, gran), _oracle(x, lens, None, T, gran),
+                     f"H={H} {gran}")

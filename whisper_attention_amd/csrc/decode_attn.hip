@@ -7,18 +7,22 @@
 // "Inference Stack") describes, with fp32 arithmetic on dequantized values.
 //
 // HBM-bound design:
-//   * grid = (b, h, key chunk); a block of 4 waves owns one chunk of one
-//     (b, h); waves take 64-key blocks round robin.
+//   * one block per (b, h) and key chunk; its W waves (1 to 8, chosen so the
+//     whole grid is resident at once, without a partly filled second round)
+//     take 64-key blocks round robin.  A chunk is the whole cache unless
+//     there are too few (b, h) pairs to fill the GPU.
 //   * lane l of a wave reads 16 bytes (16 dims) of key row l/4 of each
 //     16-key group: one dwordx4 load instruction moves 1 KB of contiguous
 //     cache, and K and V of a 64-key block are 8 such loads per lane, all
-//     issued before any use.
+//     issued before any use.  Rows past the length are never read (a lane
+//     past the end re-reads the last valid row, whose weight it zeroes).
 //   * dequantization is in registers (hardware fp8 -> fp32 pair converts);
 //     the per-head key scale, the softmax scale and log2(e) are folded into
 //     the query once, so a score is 16 FMAs plus a 4-lane DPP sum.
-//   * online softmax per wave in the exp2 domain; the 4 waves merge in LDS;
-//     chunks of one (b, h) merge in a second small kernel (skipped when a
-//     (b, h) has one chunk).
+//   * online softmax per wave in the exp2 domain, with cross-lane maxima and
+//     sums on DPP row rotations and the permlane16/32 swaps (no LDS round
+//     trips); the W waves merge in LDS; chunks of one (b, h) merge in a
+//     second small kernel (only when a (b, h) has several chunks).
 #include <algorithm>
 #include <cmath>
 
@@ -27,11 +31,11 @@
 namespace wa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+constexpr int kMaxWaves = 8;
 constexpr int kBlockKeys = 64;       // keys per wave iteration
 constexpr int kPartialStride = 68;   // o[64], m, l, pad
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaveSlots = 5120;     // resident waves: 256 CUs x 4 SIMDs x 5
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -43,7 +47,24 @@ __device__ __forceinline__ float quad_sum(float v) {
   v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
   return v;
 }
-__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
+// Fold the 16 lanes that share lane & 3 (the key rows of one dim slice):
+// rotations by 4 and 8 inside each row of 16 lanes, then the row swaps.
+__device__ __forceinline__ float rows_sum(float v) {
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(a[0]) + __int_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
 
 __device__ __forceinline__ void dequant16(const uint4 &c, float (&f)[16]) {
   uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -65,15 +86,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(5))) void decode_partial_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint8_t *__restrict__ kc,
     const uint8_t *__restrict__ vc, wa_strides cs, int cache_len, const float *__restrict__ ksc,
     const float *__restrict__ vsc, int per_head, const int32_t *__restrict__ lens, int H,
     float qmul, int chunk, int n_split, float *__restrict__ ws, uint16_t *__restrict__ o,
     wa_strides os) {
-  __shared__ float s_o[kWaves][64];
-  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float s_o[kMaxWaves][64];
+  __shared__ float s_m[kMaxWaves], s_l[kMaxWaves];
 
+  const int n_waves = blockDim.x >> 6;
   const int split = blockIdx.x % n_split;
   const int bh = blockIdx.x / n_split;
   const int b = bh / H, h = bh % H;
@@ -100,29 +122,28 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
     }
   }
 
-  const long base = (long)b * cs.b + (long)h * cs.h + qd * 16;
+  // wave-uniform bases, 32-bit per-lane offsets (the host checks that one
+  // (b, h) slab spans less than 2^31 bytes)
+  const long base = (long)b * cs.b + (long)h * cs.h;
   const uint8_t *kb = kc + base;
   const uint8_t *vb = vc + base;
+  const uint32_t ts = (uint32_t)cs.t;
 
   float m = -INFINITY, l = 0.f;
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
-  for (int blk = j0 + w * kBlockKeys; blk < j1; blk += kWaves * kBlockKeys) {
+  for (int blk = j0 + w * kBlockKeys; blk < j1; blk += n_waves * kBlockKeys) {
     uint4 kk[4], vv[4];
     bool ok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = blk + i * 16 + r;
       ok[i] = j < j1;
-      if (ok[i]) {
-        kk[i] = *reinterpret_cast<const uint4 *>(kb + (long)j * cs.t);
-        vv[i] = *reinterpret_cast<const uint4 *>(vb + (long)j * cs.t);
-      } else {
-        kk[i] = make_uint4(0, 0, 0, 0);
-        vv[i] = make_uint4(0, 0, 0, 0);
-      }
+      const uint32_t off = (uint32_t)min(j, j1 - 1) * ts + qd * 16;  // past the end: last valid row
+      kk[i] = *reinterpret_cast<const uint4 *>(kb + off);
+      vv[i] = *reinterpret_cast<const uint4 *>(vb + off);
     }
     float s[4];
 #pragma unroll
@@ -135,11 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
       acc_s = quad_sum(acc_s);
       s[i] = ok[i] ? acc_s : -INFINITY;
     }
-    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = fmaxf(bm, xor_shfl(bm, 4));
-    bm = fmaxf(bm, xor_shfl(bm, 8));
-    bm = fmaxf(bm, xor_shfl(bm, 16));
-    bm = fmaxf(bm, xor_shfl(bm, 32));
+    const float bm = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     const float m_new = fmaxf(m, bm);          // finite: key blk is valid
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
     float p[4];
@@ -159,18 +176,33 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   }
 
   // fold the 16 key rows of the wave (lanes with equal qd)
-  l += xor_shfl(l, 4);
-  l += xor_shfl(l, 8);
-  l += xor_shfl(l, 16);
-  l += xor_shfl(l, 32);
+  l = rows_sum(l);
 #pragma unroll
-  for (int d = 0; d < 16; ++d) {
-    float v = acc[d];
-    v += xor_shfl(v, 4);
-    v += xor_shfl(v, 8);
-    v += xor_shfl(v, 16);
-    v += xor_shfl(v, 32);
-    acc[d] = v;
+  for (int d = 0; d < 16; ++d) acc[d] = rows_sum(acc[d]);
+  const float vs_g = vsc[g];
+  if (n_waves == 1) {
+    // lanes 0..3 hold the whole result: dims qd*16 .. +16
+    if (r == 0) {
+      if (n_split == 1) {
+        uint16_t *op = o + (long)b * os.b + (long)h * os.h + qd * 16;
+        const float inv = l > 0.f ? vs_g / l : 0.f;
+        uint32_t wd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          wd[i] = (uint32_t)f32_to_bf16(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16(acc[2 * i + 1] * inv) << 16);
+        reinterpret_cast<uint4 *>(op)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        reinterpret_cast<uint4 *>(op)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      } else {
+        float *pw = ws + ((long)split * (gridDim.x / n_split) + bh) * kPartialStride;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) pw[qd * 16 + d] = acc[d];
+        if (qd == 0) {
+          pw[64] = m;
+          pw[65] = l;
+        }
+      }
+    }
+    return;
   }
   if (r == 0) {
 #pragma unroll
@@ -183,21 +215,19 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   __syncthreads();
   if (w != 0) return;
 
-  // merge the 4 waves: lane = output dim
+  // merge the waves: lane = output dim
   float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
+  for (int i = 0; i < n_waves; ++i) M = fmaxf(M, s_m[i]);
   float num = 0.f, den = 0.f;
   if (M != -INFINITY) {
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      const float e = s_m[i] == -INFINITY ? 0.f : exp2f(s_m[i] - M);
+    for (int i = 0; i < n_waves; ++i) {
+      const float e = s_m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[i] - M);
       num = fmaf(e, s_o[i][lane], num);
       den = fmaf(e, s_l[i], den);
     }
   }
   if (n_split == 1) {
-    const float out = den > 0.f ? num / den * vsc[g] : 0.f;
+    const float out = den > 0.f ? num / den * vs_g : 0.f;
     o[(long)b * os.b + (long)h * os.h + lane] = f32_to_bf16(out);
   } else {
     float *pw = ws + ((long)split * (gridDim.x / n_split) + bh) * kPartialStride;
@@ -238,17 +268,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restric
 }  // namespace
 
 DecodePlan decode_plan(int B, int H, int cache_len) {
-  // Aim for about 2048 blocks (8 per CU) so every CU has loads in flight;
-  // a chunk holds at least 256 keys (one 64-key block per wave).
+  // One wave per 64-key block at most, and a grid that fits in the resident
+  // wave slots at once.  Enough (b, h) pairs: one chunk each, as many waves
+  // per block as fit (up to 8).  Few pairs: split the keys into chunks of at
+  // least 256 so the GPU still has about 1024 blocks of 4 waves.
   const long bh = (long)B * H;
+  const int key_blocks = (cache_len + kBlockKeys - 1) / kBlockKeys;
+  DecodePlan p;
+  if (bh * 4 >= kWaveSlots / 2) {
+    p.n_split = 1;
+    p.chunk = key_blocks * kBlockKeys;
+    p.waves = (int)std::max<long>(1, std::min<long>(std::min(kMaxWaves, key_blocks), kWaveSlots / bh));
+    // a short cache (a decoder self-attention cache holds at most 448
+    // tokens): one 64-key block per wave, so no wave waits for two loads in
+    // a row; waves past a sequence's length exit at once
+    return p;
+  }
   const int max_split = std::max(1, (cache_len + 255) / 256);
-  int want = (int)std::min<long>(max_split, std::max<long>(1, (2048 + bh - 1) / bh));
+  const int want = (int)std::min<long>(max_split, std::max<long>(1, (1024 + bh - 1) / bh));
   int chunk = (cache_len + want - 1) / want;
   chunk = ((chunk + kBlockKeys - 1) / kBlockKeys) * kBlockKeys;
   chunk = std::max(chunk, 256);
-  DecodePlan p;
   p.chunk = chunk;
   p.n_split = std::max(1, (cache_len + chunk - 1) / chunk);
+  p.waves = std::min(4, (chunk + kBlockKeys - 1) / kBlockKeys);
   return p;
 }
 
@@ -263,7 +306,7 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
                          float softmax_scale, uint16_t *o, wa_strides os, float *ws,
                          const DecodePlan &plan, hipStream_t stream) {
   const int BH = B * H;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(BH * plan.n_split), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(BH * plan.n_split), dim3(plan.waves * 64), 0, stream,
                      q, qs, kc, vc, cs, cache_len, k_scale, v_scale, per_head, lens, H,
                      softmax_scale * kLog2e, plan.chunk, plan.n_split, ws, o, os);
   hipError_t e = hipGetLastError();

@@ -5,22 +5,27 @@
 // to the KV cache that the HF blog "Blazingly fast whisper transcriptions
 // with Inference Endpoints" (section "Inference Stack") stores in one byte.
 //
-// Grid shape shared by the two streaming kernels: block (b, c) covers rows
-// t in [c*kRows, (c+1)*kRows) of sequence b, clipped to lens[b] (one scalar
-// load per block; blocks past the length exit at once).  A row is H*64 bf16,
-// split into H*8 pieces of 16 bytes; thread p of a block owns piece p of
-// every row it visits, so its head -- and its scale group -- never changes.
+// Work split.  A row (one token of one sequence) is H*64 bf16 = P pieces of
+// 16 bytes; piece p belongs to head p/8.  A block has lcm(64, P) threads when
+// that fits in 1024 (320 for 20 heads), so it covers rows_per_pass whole rows
+// at once and thread i always owns piece i % P: its head -- its scale group
+// -- never changes, and the 8 lanes of one head sit side by side in a wave.
+// Block (b, c) handles rows [c*R, (c+1)*R) of sequence b clipped to lens[b]
+// (R = rows_per_pass * loads per thread); every load of a thread is issued
+// before the first is used.  Wider rows (P > 1024) fall back to 1024 threads
+// that loop over pieces.
 //
-//   kv_amax_kernel      register max of |bits & 0x7fff| per thread (an exact,
+//   kv_amax_kernel      max of (bits & 0x7fff) per thread -- an exact,
 //                       order-free integer max equal to the fp32 abs-max of
-//                       the bf16 values), folded per group in LDS and stored
-//                       as one partial per block and group.
-//   kv_scale_kernel     one block folds the partials and writes
-//                       scale[g] = amax_g / 448 (1 when amax_g is 0).
-//   kv_encode_kernel    reads scale[g]; each thread divides its 8 values by
-//                       it (IEEE fp32 division), clamps to +-448, converts with
-//                       the hardware OCP fp8 conversion (round to nearest
-//                       even) and writes 8 code bytes into the cache slot.
+//                       the bf16 values -- folded over the 8 lanes of a head
+//                       (or the whole wave) and in LDS, one partial per block
+//                       and group, stored group-major.
+//   kv_scale_kernel     one block per group folds that group's partials and
+//                       writes scale[g] = amax_g / 448 (1 when amax_g is 0).
+//   kv_encode_kernel    divides each value by scale[g] (IEEE fp32 division),
+//                       clamps to +-448, converts pairs with the hardware OCP
+//                       fp8 conversion (round to nearest even) and writes 8
+//                       code bytes per piece into the cache slot.
 #include <algorithm>
 
 #include "wa_internal.h"
@@ -28,8 +33,8 @@
 namespace wa {
 namespace {
 
-constexpr int kRows = 32;       // rows of one sequence per block
-constexpr int kUnroll = 8;      // loads in flight per thread
+constexpr int kAmaxLoads = 8;    // rows per thread in the amax pass
+constexpr int kEncLoads = 4;     // rows per thread in the encode pass
 
 __device__ __forceinline__ uint32_t maxabs_bits8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -64,102 +69,175 @@ __device__ __forceinline__ uint2 encode8(uint4 v, float s) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// The same 8 codes with the quotient from the reciprocal r = 1/s (IEEE) and
+// one FMA correction (Markstein): q0 = |x|*r, e = |x| - q0*s (exact in one
+// FMA), q = q0 + e*r rounded once.  For 2^-80 <= s <= 2^80 this gives the
+// correctly rounded |x|/s wherever the quotient is at least 2^-12 -- every
+// quotient that can encode to a non-zero code -- and below that both round
+// to a zero code; the sign is restored from x, so -0 stays -0.  q0 is
+// clamped first so that no step overflows.  Checked against IEEE division
+// for every finite bf16 x and every dynamic scale amax/448 in that range.
+__device__ __forceinline__ float quot_fast(float x, float s, float r) {
+  const float a = fabsf(x);
+  const float q0 = fminf(a * r, 449.0f);
+  const float e = __builtin_fmaf(-q0, s, a);
+  const float q = fminf(__builtin_fmaf(e, r, q0), 448.0f);
+  return __builtin_copysignf(q, x);
+}
+
+__device__ __forceinline__ uint2 encode8_fast(uint4 v, float s, float r) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = quot_fast(bf16_lo(w[i]), s, r);
+    y[2 * i + 1] = quot_fast(bf16_hi(w[i]), s, r);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+__device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-80f && s <= 0x1p80f; }
+
 __device__ __forceinline__ int seq_len(const int32_t *lens, int b, int T_max) {
   const int n = lens ? lens[b] : T_max;
   return min(max(n, 0), T_max);
 }
 
+// The piece and row offset a thread owns, from the block shape in QuantPlan.
+struct Lane {
+  int piece;      // first piece (of pieces_per_thread, blockDim apart)
+  int row;        // row offset inside a pass
+  bool active;
+};
+__device__ __forceinline__ Lane lane_of(int P, int rows_per_pass) {
+  Lane l;
+  const int tid = threadIdx.x;
+  if (rows_per_pass > 0) {   // blockDim is a multiple of P, or P rounded up to waves
+    l.piece = tid % P;
+    l.row = tid / P;
+    l.active = l.row < rows_per_pass;
+  } else {                   // P > blockDim: loop over pieces
+    l.piece = tid;
+    l.row = 0;
+    l.active = true;
+  }
+  return l;
+}
+
 __global__ __launch_bounds__(1024) void kv_amax_kernel(const uint16_t *__restrict__ x,
                                                        wa_strides xs, int T_max, int P,
+                                                       int rows_per_pass,
                                                        const int32_t *__restrict__ lens,
                                                        int per_head, int groups,
                                                        uint32_t *__restrict__ partial) {
   extern __shared__ uint32_t smax[];  // [groups]
   const int b = blockIdx.x;
-  const int t0 = blockIdx.y * kRows;
-  const int t1 = min(t0 + kRows, seq_len(lens, b, T_max));
+  const int rpp = max(rows_per_pass, 1);
+  const int t0 = blockIdx.y * rpp * kAmaxLoads;
+  const int t1 = min(t0 + rpp * kAmaxLoads, seq_len(lens, b, T_max));
+  const long n_blocks = (long)gridDim.x * gridDim.y;
   const long blk = (long)blockIdx.y * gridDim.x + blockIdx.x;
   for (int g = threadIdx.x; g < groups; g += blockDim.x) smax[g] = 0;
   __syncthreads();
-  if (t0 < t1) {
-    for (int p = threadIdx.x; p < P; p += blockDim.x) {
-      const uint16_t *xp = x + (long)b * xs.b + (long)(p >> 3) * xs.h + (p & 7) * 8;
-      uint32_t m = 0;
-      for (int t = t0; t < t1; t += kUnroll) {
-        uint4 v[kUnroll];
+  const Lane ln = lane_of(P, rows_per_pass);
+  const int step = rows_per_pass > 0 ? P : (int)blockDim.x;
+  for (int p = ln.piece; p < P; p += (rows_per_pass > 0 ? P : step)) {
+    const uint16_t *xp = x + (long)b * xs.b + (long)(p >> 3) * xs.h + (p & 7) * 8;
+    uint32_t m = 0;
+    if (ln.active) {
+      uint4 v[kAmaxLoads];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-          v[u] = t + u < t1 ? *reinterpret_cast<const uint4 *>(xp + (long)(t + u) * xs.t)
-                            : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) m = max(m, maxabs_bits8(v[u]));
+      for (int u = 0; u < kAmaxLoads; ++u) {
+        const int t = t0 + ln.row + u * rpp;
+        v[u] = t < t1 ? *reinterpret_cast<const uint4 *>(xp + (long)t * xs.t) : make_uint4(0, 0, 0, 0);
       }
-      atomicMax(&smax[per_head ? (p >> 3) : 0], m);
+#pragma unroll
+      for (int u = 0; u < kAmaxLoads; ++u) m = max(m, maxabs_bits8(v[u]));
     }
+    // the 8 lanes of one head are adjacent and 8-aligned (P is a multiple of 8)
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+    if ((threadIdx.x & 7) == 0 && ln.active) atomicMax(&smax[per_head ? (p >> 3) : 0], m);
+    if (rows_per_pass > 0) break;
   }
   __syncthreads();
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) partial[blk * groups + g] = smax[g];
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) partial[(long)g * n_blocks + blk] = smax[g];
 }
 
-__global__ __launch_bounds__(1024) void kv_scale_kernel(const uint32_t *__restrict__ partial,
-                                                        int n_blocks, int groups,
-                                                        float *__restrict__ scale) {
-  extern __shared__ uint32_t smax[];  // [groups]
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) smax[g] = 0;
-  __syncthreads();
-  if (groups <= (int)blockDim.x) {
-    // thread -> one group and a strided subset of the blocks' partials
-    const int per = blockDim.x / groups;
-    if ((int)threadIdx.x < per * groups) {
-      const int g = threadIdx.x % groups;
-      uint32_t m = 0;
-      for (long j = threadIdx.x / groups; j < n_blocks; j += per) m = max(m, partial[j * groups + g]);
-      atomicMax(&smax[g], m);
-    }
-  } else {
-    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-      uint32_t m = 0;
-      for (long j = 0; j < n_blocks; ++j) m = max(m, partial[j * groups + g]);
-      smax[g] = m;
-    }
+// One block per group: fold that group's n_blocks partials (contiguous).
+__global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restrict__ partial,
+                                                       int n_blocks, float *__restrict__ scale) {
+  __shared__ uint32_t wmax[4];
+  const int g = blockIdx.x;
+  const uint32_t *pg = partial + (long)g * n_blocks;
+  uint32_t m = 0;
+  int j = threadIdx.x;
+  for (; j + 768 < n_blocks; j += 1024) {
+    const uint32_t a = pg[j], b = pg[j + 256], c = pg[j + 512], d = pg[j + 768];
+    m = max(m, max(max(a, b), max(c, d)));
   }
+  for (; j < n_blocks; j += 256) m = max(m, pg[j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-    const float a = __uint_as_float(smax[g] << 16);  // bf16 bits -> fp32, exact
-    scale[g] = a == 0.0f ? 1.0f : a / 448.0f;
+  if (threadIdx.x == 0) {
+    const uint32_t a = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const float amax = __uint_as_float(a << 16);  // bf16 bits -> fp32, exact
+    scale[g] = amax == 0.0f ? 1.0f : amax / 448.0f;
   }
 }
 
 __global__ __launch_bounds__(1024) void kv_encode_kernel(
-    const uint16_t *__restrict__ x, wa_strides xs, int T_max, int P,
+    const uint16_t *__restrict__ x, wa_strides xs, int T_max, int P, int rows_per_pass,
     const int32_t *__restrict__ lens, const int32_t *__restrict__ dst_start,
     uint8_t *__restrict__ cache, wa_strides cs, int cache_len, const float *__restrict__ scale,
     int per_head) {
   const int b = blockIdx.x;
-  const int t0 = blockIdx.y * kRows;
-  const int t1 = min(t0 + kRows, seq_len(lens, b, T_max));
+  const int rpp = max(rows_per_pass, 1);
+  const int t0 = blockIdx.y * rpp * kEncLoads;
+  const int t1 = min(t0 + rpp * kEncLoads, seq_len(lens, b, T_max));
   if (t0 >= t1) return;
   const int d0 = dst_start ? dst_start[b] : 0;
   // slots outside [0, cache_len) are skipped
   const int ta = max(t0, -d0), tb = min(t1, cache_len - d0);
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+  const Lane ln = lane_of(P, rows_per_pass);
+  if (!ln.active) return;
+  for (int p = ln.piece; p < P; p += (rows_per_pass > 0 ? P : (int)blockDim.x)) {
     const int h = p >> 3;
     const float s = scale[per_head ? h : 0];
     const uint16_t *xp = x + (long)b * xs.b + (long)h * xs.h + (p & 7) * 8;
     uint8_t *cp = cache + (long)b * cs.b + (long)h * cs.h + (long)d0 * cs.t + (p & 7) * 8;
-    for (int t = ta; t < tb; t += kUnroll) {
-      uint4 v[kUnroll];
+    uint4 v[kEncLoads];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        if (t + u < tb) v[u] = *reinterpret_cast<const uint4 *>(xp + (long)(t + u) * xs.t);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        if (t + u < tb) *reinterpret_cast<uint2 *>(cp + (long)(t + u) * cs.t) = encode8(v[u], s);
+    for (int u = 0; u < kEncLoads; ++u) {
+      const int t = t0 + ln.row + u * rpp;
+      if (t >= ta && t < tb) v[u] = *reinterpret_cast<const uint4 *>(xp + (long)t * xs.t);
     }
+    if (fast_scale(s)) {
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int u = 0; u < kEncLoads; ++u) {
+        const int t = t0 + ln.row + u * rpp;
+        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8_fast(v[u], s, r);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kEncLoads; ++u) {
+        const int t = t0 + ln.row + u * rpp;
+        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8(v[u], s);
+      }
+    }
+    if (rows_per_pass > 0) break;
   }
 }
 
-int block_threads(int P) { return std::min(1024, ((P + 63) / 64) * 64); }
+int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
 }  // namespace
 
@@ -167,9 +245,22 @@ QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran) {
   QuantPlan p;
   p.pieces_per_row = H * 8;
   p.groups = gran == WA_SCALE_PER_HEAD ? H : 1;
-  p.row_chunks = (T_max + kRows - 1) / kRows;
-  p.blocks = (long)B * p.row_chunks;
-  p.threads = block_threads(p.pieces_per_row);
+  const int P = p.pieces_per_row;
+  const long l = (long)P / gcd_int(P, 64) * 64;   // lcm(64, P)
+  if (l <= 1024) {
+    p.threads = (int)l;
+    p.rows_per_pass = (int)(l / P);
+  } else if (P <= 1024) {
+    p.threads = ((P + 63) / 64) * 64;
+    p.rows_per_pass = 1;
+  } else {
+    p.threads = 1024;
+    p.rows_per_pass = 0;    // threads loop over pieces, one row per pass
+  }
+  const int rpp = std::max(p.rows_per_pass, 1);
+  p.amax_chunks = (T_max + rpp * kAmaxLoads - 1) / (rpp * kAmaxLoads);
+  p.enc_chunks = (T_max + rpp * kEncLoads - 1) / (rpp * kEncLoads);
+  p.blocks = (long)B * p.amax_chunks;
   return p;
 }
 
@@ -184,20 +275,21 @@ hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T
                            int compute_scale, uint32_t *ws, const QuantPlan &plan,
                            hipStream_t stream) {
   (void)H;
-  const dim3 grid(B, plan.row_chunks);
-  const size_t lds = (size_t)plan.groups * sizeof(uint32_t);
   if (compute_scale) {
-    hipLaunchKernelGGL(kv_amax_kernel, grid, dim3(plan.threads), lds, stream, x, xs, T_max,
-                       plan.pieces_per_row, lens, per_head, plan.groups, ws);
+    const size_t lds = (size_t)plan.groups * sizeof(uint32_t);
+    hipLaunchKernelGGL(kv_amax_kernel, dim3(B, plan.amax_chunks), dim3(plan.threads), lds, stream,
+                       x, xs, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, per_head,
+                       plan.groups, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kv_scale_kernel, dim3(1), dim3(1024), lds, stream, ws, (int)plan.blocks,
-                       plan.groups, scale);
+    hipLaunchKernelGGL(kv_scale_kernel, dim3(plan.groups), dim3(256), 0, stream, ws,
+                       (int)plan.blocks, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kv_encode_kernel, grid, dim3(plan.threads), 0, stream, x, xs, T_max,
-                     plan.pieces_per_row, lens, dst_start, cache, cs, cache_len, scale, per_head);
+  hipLaunchKernelGGL(kv_encode_kernel, dim3(B, plan.enc_chunks), dim3(plan.threads), 0, stream, x,
+                     xs, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cache,
+                     cs, cache_len, scale, per_head);
   return hipGetLastError();
 }
 

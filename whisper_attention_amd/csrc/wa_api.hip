@@ -71,7 +71,7 @@ wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_
   if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
   if (compute_scale != 0 && compute_scale != 1) return WA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64) return WA_ERR_UNSUPPORTED;
-  if (H > 8192 || (T_max + 31) / 32 > 65535) return WA_ERR_UNSUPPORTED;
+  if (H > 8192 || T_max > 65535 * 8) return WA_ERR_UNSUPPORTED;
   if (!bf16_layout_ok(x, xs) || !u8_layout_ok(cache, cs)) return WA_ERR_UNSUPPORTED;
   const wa::QuantPlan plan = wa::quant_plan(B, H, T_max, gran);
   if (compute_scale) {
@@ -126,6 +126,7 @@ wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cach
   if (!bf16_layout_ok(q, qs2) || !bf16_layout_ok(o, os2) || !u8_layout_ok(k_cache, cs) ||
       !u8_layout_ok(v_cache, cs))
     return WA_ERR_UNSUPPORTED;
+  if ((long)cache_len * cs.t > 0x7fffffffL) return WA_ERR_UNSUPPORTED;
   const wa::DecodePlan plan = wa::decode_plan(B, H, cache_len);
   if ((long)B * H * plan.n_split > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
   const size_t need = wa::decode_workspace_bytes(B, H, plan);

@@ -14,9 +14,11 @@ namespace wa {
 struct QuantPlan {
   int pieces_per_row;   // H * 8: one piece = 8 bf16 = 16 bytes
   int groups;           // 1 (per tensor) or H (per head)
-  int row_chunks;       // blocks per sequence (rows of one block: a fixed chunk)
-  long blocks;          // B * row_chunks
-  int threads;          // threads per block (pieces_per_row rounded up to waves)
+  int threads;          // threads per block
+  int rows_per_pass;    // whole rows a block covers at once (0: threads loop over pieces)
+  int amax_chunks;      // amax blocks per sequence
+  int enc_chunks;       // encode blocks per sequence
+  long blocks;          // amax blocks in all (B * amax_chunks): partials per group
 };
 QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran);
 size_t quant_workspace_bytes(const QuantPlan &p);
@@ -31,6 +33,7 @@ hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T
 struct DecodePlan {
   int n_split;          // key chunks per (b, h)
   int chunk;            // keys per chunk (multiple of 64)
+  int waves;            // waves per block (1..8)
 };
 DecodePlan decode_plan(int B, int H, int cache_len);
 size_t decode_workspace_bytes(int B, int H, const DecodePlan &p);
