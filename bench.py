@@ -38,6 +38,25 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 HEAD_DIM = 64
 N_SETS = 3                    # decode cache sets used in turn
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled
+# by what the counter reads for a plain 256 MiB copy (the commands and raw
+# counts are in profiles/hbm_traffic_counters.md), with the sha256 prefix of
+# the kernel source they were taken on: a changed kernel reports null.
+TRAFFIC = {
+    "encoder_attn.hip": ("db7713cc13134171", {"encoder": 252.4e6, "prefill": 148.5e6}),
+    "decode_attn.hip": ("85c22582c6bb3570", {"cross": 246.2e6, "self": 42.1e6}),
+}
+
+
+def traffic(source, launch):
+    import hashlib
+    sha, values = TRAFFIC[source]
+    path = os.path.join(ROOT, "whisper_attention_amd", "csrc", source)
+    with open(path, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
+            return None
+    return values[launch]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -290,11 +309,16 @@ def main():
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "roofline": {"bound": "mfma", "kernel": "encoder_attn_kernel",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic("encoder_attn.hip", "encoder"), "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": 4 * 2.0 * wl.enc["B"] * wl.enc["H"] * wl.enc["T"] * HEAD_DIM},
         "roofline_decode": {"bound": "hbm", "kernel": "decode_partial_kernel",
                             "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                            "context": "inside the step"},
+                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": (None if traffic("decode_attn.hip", "cross") is None else
+                                        traffic("decode_attn.hip", "cross") + traffic("decode_attn.hip", "self")),
+                            "traffic_unit": "bytes per decode step (cross + self launch)",
+                            "algorithmic_bytes": bx + bs, "context": "inside the step"},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -55,6 +55,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -90,8 +91,8 @@ __device__ __forceinline__ int swap_bits23(int m) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // v_cvt_pk_bf16_f32: round to nearest even
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 __device__ __forceinline__ float max_with_lane_xor32(float x) {
   // v_permlane32_swap: each lane gets its own value and that of lane ^ 32
@@ -209,6 +210,28 @@ __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
   }
 }
 
+// P = exp2(S*c - m) for one tile, as bf16 P^T operands.
+__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][2], const float (&m)[2],
+                                            float c_log2, bf16x8 (&pb)[2][4]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mneg = -m[qb];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
+          wd[i] = pack_bf16x2(p0, p1);
+        }
+        pb[qb][kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+      }
+  }
+}
+
 // Online softmax of one tile's scores (vector ALU only): mask, tile max,
 // lazy rescale of O and l, P = exp2(S*c - m) as bf16 P^T operands, row sums.
 template <bool kCausal>
@@ -261,22 +284,14 @@ __device__ __forceinline__ void softmax_tile(WaveState &st, f32x16 (&s)[2][2], i
       st.m_run[qb] = m_new;
     }
   }
+  // The exponentials go to the transcendental unit at a quarter of the FMA
+  // rate; the scheduling groups interleave them with the FMAs and
+  // conversions, which then issue in their shadow instead of before them.
+  softmax_exp(s, st.m_run, c_log2, pb);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float mneg = -st.m_run[qb];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i], c_log2, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][hh * 8 + 2 * i + 1], c_log2, mneg));
-          wd[i] = pack_bf16x2(p0, p1);
-        }
-        pb[qb][kb * 2 + hh] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-      }
+  for (int g = 0; g < 64; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
   }
 }
 
