@@ -49,7 +49,8 @@ def _check(got, q, k, v, lens, causal, what, pairs=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,T,lens", [(2, 3, 300, [300, 131]), (3, 2, 77, [77, 1, 64]),
-                                        (1, 1, 1, [1]), (2, 2, 129, [0, 129]), (1, 2, 128, [128])])
+                                        (1, 1, 1, [1]), (2, 2, 129, [0, 129]), (1, 2, 128, [128]),
+                                        (1, 2, 256, [256]), (2, 1, 257, [257, 250])])
 def test_ragged_shapes(gpu, B, H, T, lens, causal):
     import whisper_attention_amd as wa
     announce(f"encoder ragged B={B} H={H} T={T} lens={lens} causal={causal}")

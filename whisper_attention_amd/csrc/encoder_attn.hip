@@ -59,10 +59,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 8;                 // two groups of four
-constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 64;                   // queries per wave (two 32-query MFMA blocks)
-constexpr int kBM = kWaves * kQW;         // queries per block
+constexpr int kGroupQueries = 4 * kQW;    // queries of one group of four waves
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
 constexpr int kStageBytes = 2 * kTileBytes;  // K then V
@@ -72,7 +70,6 @@ constexpr float kLazy = 8.0f;             // lazy-rescale threshold, log2 units
 // in 6:4, lgkmcnt in 11:8): wait until at most N vector-memory operations of
 // this wave are outstanding and all its LDS operations are complete.
 constexpr int kVmcnt0Lgkm0 = 0x0070;
-constexpr int kVmcnt2Lgkm0 = 0x0072;
 
 // 16-byte chunk swizzle of a 128-byte LDS row: the chunk index is XORed with
 // bits 1, 2, 3 of the row, reversed.  The K operand reads (16 rows, one chunk)
@@ -101,18 +98,18 @@ __device__ __forceinline__ float max_with_lane_xor32(float x) {
 }
 
 // Per-lane byte offsets of the K (and V) row this lane copies in every
-// tile, relative to the tile's first row: wave w copies rows [8w, 8w+8);
-// lane l lands in 16-byte LDS slot l of the instruction's 1 KB and fetches
-// the global chunk the swizzle assigns to that slot.  Rows at or past kend
-// are clamped to row kend-1 (finite data; their scores are masked to -inf, so
-// they carry zero weight).
+// tile, relative to the tile's first row: one copy instruction fills rows
+// [row0, row0+8); lane l lands in 16-byte LDS slot l of the instruction's
+// 1 KB and fetches the global chunk the swizzle assigns to that slot.  Rows
+// at or past kend are clamped to row kend-1 (finite data; their scores are
+// masked to -inf, so they carry zero weight).
 struct CopyOffsets {
   uint32_t k, v;
 };
 
 __device__ __forceinline__ CopyOffsets copy_offsets(wa_strides ks, wa_strides vs, int max_row,
-                                                    int lane, int w) {
-  const int row = w * 8 + (lane >> 3);
+                                                    int lane, int row0) {
+  const int row = row0 + (lane >> 3);
   const int chunk = (lane & 7) ^ swz(row);
   const int r = min(row, max_row);
   return CopyOffsets{(uint32_t)((r * ks.t + chunk * 8) * 2), (uint32_t)((r * vs.t + chunk * 8) * 2)};
@@ -143,15 +140,21 @@ __device__ __forceinline__ uint32_t lds_addr(int stage) {
 }
 
 // Issue the asynchronous copy of the K/V tile that starts at row k0 into a
-// stage.  Wave w fills K rows and V rows [8w, 8w+8) of the stage.
+// stage.  Wave w fills K rows and V rows [8*kCopies*w, 8*kCopies*(w+1)) of
+// the stage, 8 rows per copy instruction.
+template <int kCopies>
 __device__ __forceinline__ void issue_tile(int stage, const uint16_t *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
-                                           const CopyOffsets &full, int lane, int w) {
-  // only the last tile can run past kend
-  const CopyOffsets c = k0 + kBN <= kend ? full : copy_offsets(ks, vs, kend - 1 - k0, lane, w);
-  const uint32_t dst = lds_addr(stage) + w * 8 * 128;
-  copy16_to_lds(kp + (long)k0 * ks.t, c.k, dst);
-  copy16_to_lds(vp + (long)k0 * vs.t, c.v, dst + kTileBytes);
+                                           const CopyOffsets (&full)[kCopies], int lane, int w) {
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int row0 = (w * kCopies + i) * 8;
+    // only the last tile can run past kend
+    const CopyOffsets c = k0 + kBN <= kend ? full[i] : copy_offsets(ks, vs, kend - 1 - k0, lane, row0);
+    const uint32_t dst = lds_addr(stage) + row0 * 128;
+    copy16_to_lds(kp + (long)k0 * ks.t, c.k, dst);
+    copy16_to_lds(vp + (long)k0 * vs.t, c.v, dst + kTileBytes);
+  }
 }
 
 // Per-wave state of the online softmax.
@@ -337,10 +340,11 @@ __device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
   }
 }
 
+template <int kCopies>
 struct Ctx {
   const uint16_t *kp, *vp;
   wa_strides ks, vs;
-  CopyOffsets co;
+  CopyOffsets co[kCopies];
   ReadOffsets ro;
   int nt, kend, len, wq_lo, lane, w, group;
   float c_log2;
@@ -349,41 +353,44 @@ struct Ctx {
 // Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+2 is
 // copied into `ahead` (the stage of tile t-2, whose last reads were in
 // interval t-1).  Both groups pass the same barriers, one per interval.
-__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx &x) {
+template <int kCopies>
+__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx<kCopies> &x) {
   // Keep every instruction of the previous interval above the barrier: the
   // scheduler would otherwise sink matrix instructions (they touch no memory)
   // past it and break the two groups' phase alignment.
   __builtin_amdgcn_sched_barrier(0);
-  // This wave's copies of tile t are complete -- only tile t+1's two copies
-  // may still be in flight -- and so are its LDS reads of interval t-1.  Then
+  // This wave's copies of tile t are complete -- only tile t+1's 2*kCopies
+  // copies may still be in flight -- and so are its LDS reads of interval
+  // t-1 (the immediate holds vmcnt in bits 3:0 and lgkmcnt 0).  Then
   // a bare barrier (a workgroup fence would wait for tile t+1's copies too):
   // afterwards tile t is in LDS for everyone and the stage of tile t-2 is free.
   if (t + 1 < x.nt)
-    __builtin_amdgcn_s_waitcnt(kVmcnt2Lgkm0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0 + 2 * kCopies);
   else
     __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if (t + 2 < x.nt) issue_tile(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
+  if (t + 2 < x.nt)
+    issue_tile<kCopies>(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
-template <bool kCausal>
-__device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
+template <bool kCausal, int kCopies>
+__device__ __forceinline__ bool wave_needs(int j, const Ctx<kCopies> &x) {
   return j >= 0 && j < x.nt && !(kCausal && j * kBN > x.wq_lo + kQW - 1);
 }
 
 // Group A: P(t-1).V(t-1) and S(t) on the matrix cores, then softmax(t);
 // P(t) is carried to the next interval.
-template <bool kCausal>
+template <bool kCausal, int kCopies>
 __device__ __forceinline__ void interval_a(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
                                            const uint8_t *prev, int ahead, int t,
-                                           const Ctx &x) {
+                                           const Ctx<kCopies> &x) {
   open_interval(ahead, t, x);
-  if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
-  if (wave_needs<kCausal>(t, x)) {
+  if (wave_needs<kCausal, kCopies>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
+  if (wave_needs<kCausal, kCopies>(t, x)) {
     f32x16 s[2][2];
     scores(st, cur, x.ro, s);
     __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
@@ -393,22 +400,25 @@ __device__ __forceinline__ void interval_a(WaveState &st, bf16x8 (&pa)[2][4], co
 
 // Group B: softmax(t-1) of the carried S(t-1) first, then P(t-1).V(t-1) and
 // S(t) on the matrix cores; S(t) is carried to the next interval.
-template <bool kCausal>
+template <bool kCausal, int kCopies>
 __device__ __forceinline__ void interval_b(WaveState &st, f32x16 (&sb)[2][2], const uint8_t *cur,
                                            const uint8_t *prev, int ahead, int t,
-                                           const Ctx &x) {
+                                           const Ctx<kCopies> &x) {
   open_interval(ahead, t, x);
-  if (wave_needs<kCausal>(t - 1, x)) {
+  if (wave_needs<kCausal, kCopies>(t - 1, x)) {
     bf16x8 pb[2][4];
     softmax_tile<kCausal>(st, sb, (t - 1) * kBN, x.len, x.wq_lo, x.c_log2, x.lane, pb);
     __builtin_amdgcn_sched_barrier(0);  // vector phase, then matrix phase
     accumulate_pv(st, prev + kTileBytes, x.ro, pb);
   }
-  if (wave_needs<kCausal>(t, x)) scores(st, cur, x.ro, sb);
+  if (wave_needs<kCausal, kCopies>(t, x)) scores(st, cur, x.ro, sb);
 }
 
-template <bool kCausal>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+// kGroups = 2: eight waves in two ping-pong groups, 512 queries per block.
+// kGroups = 1: group A alone, four waves and 256 queries per block (short
+// sequences: two such blocks share a CU and interleave on their own).
+template <bool kCausal, int kGroups>
+__global__ __launch_bounds__(kGroups * 256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
@@ -423,13 +433,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   if (kCausal) qt = n_qt - 1 - qt;  // longest rows first
   const int b = bh / H, h = bh - b * H;
   const int len = min(max(lens ? lens[b] : T_max, 0), T_max);
+  constexpr int kBM = kGroups * kGroupQueries;
+  constexpr int kCopies = 2 / kGroups;   // 8-row copy instructions per wave per K/V tile
   const int q0 = qt * kBM;
   if (q0 >= len) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int group = w >> 2;
-  Ctx x;
+  Ctx<kCopies> x;
   x.kp = k + (long)b * ks.b + (long)h * ks.h;
   x.vp = v + (long)b * vs.b + (long)h * vs.h;
   x.ks = ks;
@@ -438,14 +450,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   x.nt = (x.kend + kBN - 1) / kBN;
   x.len = len;
   // group A holds queries [q0, q0+256), group B [q0+256, q0+512)
-  x.wq_lo = q0 + group * 4 * kQW + (w & 3) * kQW;
+  x.wq_lo = q0 + group * kGroupQueries + (w & 3) * kQW;
   x.lane = lane;
   x.w = w;
   x.group = group;
   x.c_log2 = c_log2;
-  x.co = copy_offsets(ks, vs, kBN - 1, lane, w);
-  issue_tile(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
-  if (x.nt > 1) issue_tile(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopies + i) * 8);
+  issue_tile<kCopies>(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
+  if (x.nt > 1) issue_tile<kCopies>(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
   x.ro = read_offsets(lane);
 
   WaveState st;
@@ -471,27 +484,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   // intervals t = 0 .. nt: tile t's K and tile t-1's V; the stage of tile j
   // is j % 4.  Each group runs its own loop (its carried operands stay in
   // registers); both pass one barrier per interval.
-  if (group == 0) {
+  if (kGroups == 1 || group == 0) {
     bf16x8 pa[2][4];
     for (int t = 0; t <= x.nt; t += 4) {
-      interval_a<kCausal>(st, pa, g_lds[0], g_lds[3], 2, t, x);
+      interval_a<kCausal, kCopies>(st, pa, g_lds[0], g_lds[3], 2, t, x);
       if (t + 1 > x.nt) break;
-      interval_a<kCausal>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
+      interval_a<kCausal, kCopies>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
       if (t + 2 > x.nt) break;
-      interval_a<kCausal>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
+      interval_a<kCausal, kCopies>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
       if (t + 3 > x.nt) break;
-      interval_a<kCausal>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
+      interval_a<kCausal, kCopies>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
     }
   } else {
     f32x16 sb[2][2];
     for (int t = 0; t <= x.nt; t += 4) {
-      interval_b<kCausal>(st, sb, g_lds[0], g_lds[3], 2, t, x);
+      interval_b<kCausal, kCopies>(st, sb, g_lds[0], g_lds[3], 2, t, x);
       if (t + 1 > x.nt) break;
-      interval_b<kCausal>(st, sb, g_lds[1], g_lds[0], 3, t + 1, x);
+      interval_b<kCausal, kCopies>(st, sb, g_lds[1], g_lds[0], 3, t + 1, x);
       if (t + 2 > x.nt) break;
-      interval_b<kCausal>(st, sb, g_lds[2], g_lds[1], 0, t + 2, x);
+      interval_b<kCausal, kCopies>(st, sb, g_lds[2], g_lds[1], 0, t + 2, x);
       if (t + 3 > x.nt) break;
-      interval_b<kCausal>(st, sb, g_lds[3], g_lds[2], 1, t + 3, x);
+      interval_b<kCausal, kCopies>(st, sb, g_lds[3], g_lds[2], 1, t + 3, x);
     }
   }
 
@@ -526,17 +539,27 @@ hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, w
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
                           int H, int T_max, const int32_t *lens, int causal,
                           float softmax_scale, hipStream_t stream) {
-  const int n_qt = (T_max + kBM - 1) / kBM;
+  const float c_log2 = softmax_scale * kLog2e;
+  // short sequences (a decoder prompt) fit one four-wave group
+  const int groups = T_max <= kGroupQueries ? 1 : 2;
+  const int n_qt = (T_max + groups * kGroupQueries - 1) / (groups * kGroupQueries);
   const long total = (long)B * H * n_qt;
-  const long grid = (total + 7) / 8 * 8;
-  if (causal)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q,
-                       qs, k, ks, v, vs, o, os, H, T_max, lens, softmax_scale * kLog2e, n_qt,
-                       (int)total);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q,
-                       qs, k, ks, v, vs, o, os, H, T_max, lens, softmax_scale * kLog2e, n_qt,
-                       (int)total);
+  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(groups * 256);
+  if (causal) {
+    if (groups == 1)
+      hipLaunchKernelGGL((attn_fwd_kernel<true, 1>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
+                         os, H, T_max, lens, c_log2, n_qt, (int)total);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<true, 2>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
+                         os, H, T_max, lens, c_log2, n_qt, (int)total);
+  } else {
+    if (groups == 1)
+      hipLaunchKernelGGL((attn_fwd_kernel<false, 1>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
+                         os, H, T_max, lens, c_log2, n_qt, (int)total);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<false, 2>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
+                         os, H, T_max, lens, c_log2, n_qt, (int)total);
+  }
   return hipGetLastError();
 }
 
