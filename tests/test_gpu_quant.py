@@ -192,3 +192,16 @@ def test_head_counts_and_block_shapes(gpu, H):
     for gran in ("tensor", "head"):
         _assert_same(_run_quant(wa, x, lens, None, T, gran), _oracle(x, lens, None, T, gran),
                      f"H={H} {gran}")
+
+
+def test_dynamic_scale_long_rows_one_head(gpu):
+    """A dynamic scale over 139001 rows of one head: a large grid of amax
+    blocks, so the scale kernel folds thousands of partials per group."""
+    import whisper_attention_amd as wa
+    B, T, H = 2, 70000, 1
+    announce(f"quant dynamic scale, B={B} T={T} H={H} (many partials)")
+    x = workloads.bf16_normal((B, T, H, 64), 10, 83, 0.01, 20.0)
+    lens = [70000, 69001]
+    for gran in ("tensor", "head"):
+        _assert_same(_run_quant(wa, x, lens, None, T, gran), _oracle(x, lens, None, T, gran),
+                     f"long rows {gran}")
