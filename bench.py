@@ -116,6 +116,9 @@ class Workload:
         self.lens_s = torch.from_numpy(self.lens_s_host).to(dev)
         self.lens_x = torch.full((B,), Lx, dtype=torch.int32, device=dev)
         self.qd = gen_bf16((B, H, HEAD_DIM), g)
+        self.kn = gen_bf16((B, H, HEAD_DIM), g)      # a decode step's new token
+        self.vn = gen_bf16((B, H, HEAD_DIM), g)
+        self.od_a = torch.empty_like(self.qd)
         self.od_x = torch.empty_like(self.qd)
         self.od_s = torch.empty_like(self.qd)
         # N_SETS independent cache sets, used in turn, so that every decode
@@ -174,6 +177,13 @@ class Workload:
         wa.wa_decode_attn(self.qd, sk, sv, sks, svs, self.lens_s, "tensor", 0.125, out=self.od_s,
                           workspace=self.ws_ds)
         rec(j + 2)
+
+    def decode_append(self, i):
+        """Self-attention with the step's token appended, one launch."""
+        caches = self.sets[i % N_SETS]
+        (sk, sks), (sv, svs) = caches["sk"], caches["sv"]
+        self.wa.wa_decode_attn_append(self.qd, self.kn, self.vn, sk, sv, sks, svs, self.lens_s,
+                                      "tensor", 0.125, out=self.od_a, workspace=self.ws_ds)
 
     def run(self, i, ev=None):
         """Step i; ``ev`` (list of 6 events) brackets the kernels."""
@@ -245,13 +255,16 @@ def main():
     # The decode calls once more on their own: in the step they follow the
     # prefill kernels, whose freshly written outputs the last-level cache
     # writes back to HBM during the decode reads.
-    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(N_SETS):
         wl.decode(i, lambda j: None, 0)
+        wl.decode_append(i)
     for i in range(args.steps):
         wl.decode(i, lambda j, e=devs[i]: e[j].record(), 0)
+        wl.decode_append(i)
+        devs[i][3].record()
     torch.cuda.synchronize()
-    dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(2)] for i in range(args.steps)])
+    dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
     if args.copy_calib:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -301,6 +314,11 @@ def main():
                               "self_GBps": round(bs / (dms[1] * 1e-3) / 1e9, 1),
                               "us": [round(dms[0] * 1e3, 2), round(dms[1] * 1e3, 2)],
                               "context": f"decode calls back to back, {N_SETS} cache sets in turn"},
+        "decode_self_append": {"value": round((bs + 2.0 * wl.dec["B"] * wl.dec["H"] * HEAD_DIM * 2)
+                                              / (dms[2] * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "us": round(dms[2] * 1e3, 2),
+                               "context": "self-attention step with the new token's K/V encoded into "
+                                          "slot len-1 in the same launch (decode-alone loop)"},
         "encoder_attn": {"value": round(enc_tflops, 2), "unit": "TFLOP/s",
                          "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4), "us": round(ms[0] * 1e3, 2)},
         "kv_quant": {"value": round(quant_gbps, 1), "unit": "GB/s",

@@ -161,6 +161,35 @@ wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cach
 
 size_t wa_decode_attn_workspace_size(int B, int H, int cache_len);
 
+/*
+ * wa_decode_attn_append -- one decoder self-attention step that also appends
+ * the step's token to the cache, in one launch.
+ *
+ * What: the decode-step append of the HF blog's float8 KV cache ("Blazingly
+ *   fast whisper transcriptions with Inference Endpoints", section
+ *   "Inference Stack": each new token's keys and values are stored in one
+ *   byte) followed by whisper-blaze's decoder_self_attn for that token
+ *   (whisper-blaze 0.1.8, "Direct Kernel API").  Per sequence b and head h,
+ *   with n = lens[b] clamped to [0, cache_len] and n counting the new token:
+ *     Kc[b,h,n-1] = E4M3(k_new[b,h] / k_scale[g]),  Vc[b,h,n-1] likewise,
+ *   exactly the codes wa_kv_quant_fp8 with compute_scale = 0 and
+ *   dst_start = n - 1 writes; then o as in wa_decode_attn over the n slots.
+ *   Slots other than n - 1 are read, never written.  n = 0 writes nothing
+ *   and gives a zero row.
+ *
+ * k_new, v_new  device bf16 [B][H][64], strides ns (ns.b, ns.h; ns.t ignored).
+ * k_cache, v_cache  device uint8 [B][H][cache_len][64], written at slot n-1.
+ * Other arguments, the workspace (wa_decode_attn_workspace_size) and the
+ * errors are those of wa_decode_attn.
+ */
+wa_status wa_decode_attn_append(const uint16_t *q, wa_strides qs, const uint16_t *k_new,
+                                const uint16_t *v_new, wa_strides ns, uint8_t *k_cache,
+                                uint8_t *v_cache, wa_strides cs, int cache_len,
+                                const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                                const int32_t *lens, int B, int H, int head_dim,
+                                float softmax_scale, uint16_t *o, wa_strides os, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *wa_status_string(wa_status s);
 

@@ -138,3 +138,25 @@ def test_valid_call_without_device_reports_hip_error(wa):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible: a valid call with fake pointers would launch")
     assert _enc(wa) == wa.WA_ERR_HIP
+
+
+def _app(wa, **kw):
+    cs = wa.Strides(20 * 1500 * 64, 64, 1500 * 64)
+    ts = wa.Strides(20 * 64, 0, 64)
+    a = dict(q=FAKE, qs=ts, kn=FAKE, vn=FAKE, ns=ts, kc=FAKE, vc=FAKE, cs=cs, L=1500, ks=FAKE, vs=FAKE,
+             gran=0, lens=FAKE, B=1, H=6, D=64, sc=0.125, o=FAKE, os=ts, ws=FAKE, wsb=0)
+    a.update(kw)
+    return wa.lib.wa_decode_attn_append(a["q"], a["qs"], a["kn"], a["vn"], a["ns"], a["kc"], a["vc"],
+                                        a["cs"], a["L"], a["ks"], a["vs"], a["gran"], a["lens"], a["B"],
+                                        a["H"], a["D"], a["sc"], a["o"], a["os"], a["ws"], a["wsb"], None)
+
+
+def test_decode_append_validation(wa):
+    for name in ("q", "kn", "vn", "kc", "vc", "ks", "vs", "lens", "o"):
+        assert _app(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _app(wa, B=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _app(wa, D=128) == wa.WA_ERR_UNSUPPORTED
+    assert _app(wa, kn=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _app(wa, ns=wa.Strides(20 * 64, 0, 12)) == wa.WA_ERR_UNSUPPORTED
+    assert _app(wa, ws=None) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _app(wa, wsb=64) == wa.WA_ERR_WORKSPACE_TOO_SMALL

@@ -55,6 +55,8 @@ def _load():
     lib.wa_encoder_attn.restype = I
     lib.wa_decode_attn.argtypes = [P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
     lib.wa_decode_attn.restype = I
+    lib.wa_decode_attn_append.argtypes = [P, S, P, P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
+    lib.wa_decode_attn_append.restype = I
     lib.wa_decode_attn_workspace_size.argtypes = [I, I, I]
     lib.wa_decode_attn_workspace_size.restype = Z
     lib.wa_status_string.argtypes = [I]
@@ -65,7 +67,8 @@ def _load():
 lib = _load()
 
 EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn",
-            "wa_decode_attn", "wa_decode_attn_workspace_size", "wa_status_string")
+            "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
+            "wa_status_string")
 
 
 def wa_status_string(status):
@@ -187,4 +190,34 @@ def wa_decode_attn(q, k_cache, v_cache, k_scale, v_scale, lens, gran, softmax_sc
                               _cache_strides(k_cache), L, _ptr(k_scale), _ptr(v_scale),
                               _gran(gran), _ptr(lens), B, H, D, float(softmax_scale), _ptr(out),
                               _tok_strides(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def wa_decode_attn_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, lens, gran,
+                          softmax_scale=0.125, out=None, workspace=None, stream=None):
+    """Append the step's token (k_new, v_new: [B][H][64] bf16) to the uint8
+    caches at slot lens[b] - 1 with the stored scales, then attend q to the
+    lens[b] slots, in one launch."""
+    for t in (q, k_new, v_new):
+        _bits(t, torch.bfloat16)
+    _bits(k_cache, torch.uint8)
+    _bits(v_cache, torch.uint8)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_new.stride() != v_new.stride() or k_new.shape != q.shape or v_new.shape != q.shape:
+        raise ValueError("k_new and v_new must have q's shape and share strides")
+    B, H, D = q.shape
+    L = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = wa_decode_attn_workspace_size(B, H, L)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wa_decode_attn_append(_ptr(q), _tok_strides(q), _ptr(k_new), _ptr(v_new),
+                                     _tok_strides(k_new), _ptr(k_cache), _ptr(v_cache),
+                                     _cache_strides(k_cache), L, _ptr(k_scale), _ptr(v_scale),
+                                     _gran(gran), _ptr(lens), B, H, D, float(softmax_scale),
+                                     _ptr(out), _tok_strides(out), _ptr(workspace), ws_bytes,
+                                     _stream(q, stream)))
     return out

@@ -26,6 +26,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "e4m3_encode.h"
 #include "wa_internal.h"
 
 namespace wa {
@@ -86,12 +87,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// kAppend: the new token's K and V (bf16 k_new, v_new [B][H][64]) are
+// encoded with the stored scales into slot lens[b] - 1 of the caches and
+// attended to from registers; every other wave and block reads only the
+// slots before it, so nothing reads the slot while it is written.
+template <bool kAppend>
 __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(5))) void decode_partial_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint8_t *__restrict__ kc,
     const uint8_t *__restrict__ vc, wa_strides cs, int cache_len, const float *__restrict__ ksc,
     const float *__restrict__ vsc, int per_head, const int32_t *__restrict__ lens, int H,
     float qmul, int chunk, int n_split, float *__restrict__ ws, uint16_t *__restrict__ o,
-    wa_strides os) {
+    wa_strides os, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    wa_strides ns) {
   __shared__ float s_o[kMaxWaves][64];
   __shared__ float s_m[kMaxWaves], s_l[kMaxWaves];
 
@@ -105,7 +112,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   const int n = min(max(lens[b], 0), cache_len);
   const int j0 = split * chunk;
-  const int j1 = min(j0 + chunk, n);
+  // with kAppend the last slot, n - 1, is the new token's, handled apart
+  const int j1 = min(j0 + chunk, kAppend ? n - 1 : n);
 
   // query slice (dims qd*16 .. qd*16+15), pre-multiplied by
   // softmax_scale * k_scale * log2(e) so scores come out in the exp2 domain
@@ -172,6 +180,43 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int d = 0; d < 16; ++d) acc[d] = fmaf(p[i], f[d], acc[d]);
     }
+    m = m_new;
+  }
+
+  if (kAppend && w == 0 && n > 0 && (n - 1) / chunk == split) {
+    // encode the new token's K and V rows into slot n - 1 (lanes 0..3 each
+    // hold 16 dims), then one more online-softmax step with that row alone
+    const int slot = n - 1;
+    const float sk = ksc[g], sv = vsc[g];
+    uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+    if (r == 0) {
+      const long src = (long)b * ns.b + (long)h * ns.h + qd * 16;
+      const uint4 *kp = reinterpret_cast<const uint4 *>(k_new + src);
+      const uint4 *vp = reinterpret_cast<const uint4 *>(v_new + src);
+      const uint2 k0 = encode8_scaled(kp[0], sk, 1.0f / sk, fast_scale(sk));
+      const uint2 k1 = encode8_scaled(kp[1], sk, 1.0f / sk, fast_scale(sk));
+      const uint2 v0 = encode8_scaled(vp[0], sv, 1.0f / sv, fast_scale(sv));
+      const uint2 v1 = encode8_scaled(vp[1], sv, 1.0f / sv, fast_scale(sv));
+      kn = make_uint4(k0.x, k0.y, k1.x, k1.y);
+      vn = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      const long dst = (long)b * cs.b + (long)h * cs.h + (long)slot * cs.t + qd * 16;
+      *reinterpret_cast<uint4 *>(const_cast<uint8_t *>(kc) + dst) = kn;
+      *reinterpret_cast<uint4 *>(const_cast<uint8_t *>(vc) + dst) = vn;
+    }
+    float f[16];
+    dequant16(kn, f);
+    float sn = 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) sn = fmaf(qf[d], f[d], sn);
+    sn = quad_sum(sn);
+    if (r != 0) sn = -INFINITY;
+    const float m_new = fmaxf(m, rows_max(sn));
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float p = __builtin_amdgcn_exp2f(sn - m_new);   // 0 outside lanes 0..3
+    l = l * alpha + p;
+    dequant16(vn, f);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = fmaf(p, f[d], acc[d] * alpha);
     m = m_new;
   }
 
@@ -304,11 +349,17 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
                          wa_strides cs, int cache_len, const float *k_scale,
                          const float *v_scale, int per_head, const int32_t *lens, int B, int H,
                          float softmax_scale, uint16_t *o, wa_strides os, float *ws,
-                         const DecodePlan &plan, hipStream_t stream) {
+                         const DecodePlan &plan, hipStream_t stream, const uint16_t *k_new,
+                         const uint16_t *v_new, wa_strides ns) {
   const int BH = B * H;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(BH * plan.n_split), dim3(plan.waves * 64), 0, stream,
-                     q, qs, kc, vc, cs, cache_len, k_scale, v_scale, per_head, lens, H,
-                     softmax_scale * kLog2e, plan.chunk, plan.n_split, ws, o, os);
+  if (k_new)
+    hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(BH * plan.n_split), dim3(plan.waves * 64), 0,
+                       stream, q, qs, kc, vc, cs, cache_len, k_scale, v_scale, per_head, lens, H,
+                       softmax_scale * kLog2e, plan.chunk, plan.n_split, ws, o, os, k_new, v_new, ns);
+  else
+    hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(BH * plan.n_split), dim3(plan.waves * 64), 0,
+                       stream, q, qs, kc, vc, cs, cache_len, k_scale, v_scale, per_head, lens, H,
+                       softmax_scale * kLog2e, plan.chunk, plan.n_split, ws, o, os, k_new, v_new, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_split == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(BH), dim3(64), 0, stream, ws, BH, H, plan.n_split,

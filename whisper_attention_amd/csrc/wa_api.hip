@@ -110,22 +110,28 @@ size_t wa_decode_attn_workspace_size(int B, int H, int cache_len) {
   return wa::decode_workspace_bytes(B, H, wa::decode_plan(B, H, cache_len));
 }
 
-wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
-                         const uint8_t *v_cache, wa_strides cs, int cache_len,
-                         const float *k_scale, const float *v_scale, wa_scale_gran gran,
-                         const int32_t *lens, int B, int H, int head_dim, float softmax_scale,
-                         uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+wa_status decode_common(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                        const uint8_t *v_cache, wa_strides cs, int cache_len,
+                        const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                        const int32_t *lens, int B, int H, int head_dim, float softmax_scale,
+                        uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream, const uint16_t *k_new, const uint16_t *v_new,
+                        wa_strides ns) {
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !lens || !o)
     return WA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
   if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64) return WA_ERR_UNSUPPORTED;
-  wa_strides qs2 = {qs.b, 0, qs.h}, os2 = {os.b, 0, os.h};
+  wa_strides qs2 = {qs.b, 0, qs.h}, os2 = {os.b, 0, os.h}, ns2 = {ns.b, 0, ns.h};
   if (!bf16_layout_ok(q, qs2) || !bf16_layout_ok(o, os2) || !u8_layout_ok(k_cache, cs) ||
       !u8_layout_ok(v_cache, cs))
     return WA_ERR_UNSUPPORTED;
+  if (k_new && (!bf16_layout_ok(k_new, ns2) || !bf16_layout_ok(v_new, ns2))) return WA_ERR_UNSUPPORTED;
   if ((long)cache_len * cs.t > 0x7fffffffL) return WA_ERR_UNSUPPORTED;
   const wa::DecodePlan plan = wa::decode_plan(B, H, cache_len);
   if ((long)B * H * plan.n_split > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
@@ -139,7 +145,36 @@ wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cach
   if (st != WA_OK) return st;
   return from_hip(wa::launch_decode(q, qs2, k_cache, v_cache, cs, cache_len, k_scale, v_scale,
                                     gran == WA_SCALE_PER_HEAD, lens, B, H, softmax_scale, o, os2,
-                                    static_cast<float *>(workspace), plan, stream));
+                                    static_cast<float *>(workspace), plan, stream, k_new, v_new,
+                                    ns2));
+}
+
+}  // namespace
+
+extern "C" {
+
+wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                         const uint8_t *v_cache, wa_strides cs, int cache_len,
+                         const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                         const int32_t *lens, int B, int H, int head_dim, float softmax_scale,
+                         uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return decode_common(q, qs, k_cache, v_cache, cs, cache_len, k_scale, v_scale, gran, lens, B,
+                       H, head_dim, softmax_scale, o, os, workspace, workspace_bytes, stream,
+                       nullptr, nullptr, wa_strides{0, 0, 0});
+}
+
+wa_status wa_decode_attn_append(const uint16_t *q, wa_strides qs, const uint16_t *k_new,
+                                const uint16_t *v_new, wa_strides ns, uint8_t *k_cache,
+                                uint8_t *v_cache, wa_strides cs, int cache_len,
+                                const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                                const int32_t *lens, int B, int H, int head_dim,
+                                float softmax_scale, uint16_t *o, wa_strides os, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!k_new || !v_new) return WA_ERR_INVALID_ARGUMENT;
+  return decode_common(q, qs, k_cache, v_cache, cs, cache_len, k_scale, v_scale, gran, lens, B,
+                       H, head_dim, softmax_scale, o, os, workspace, workspace_bytes, stream,
+                       k_new, v_new, ns);
 }
 
 }  // extern "C"

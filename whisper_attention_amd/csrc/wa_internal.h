@@ -42,7 +42,9 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
                          wa_strides cs, int cache_len, const float *k_scale,
                          const float *v_scale, int per_head, const int32_t *lens, int B, int H,
                          float softmax_scale, uint16_t *o, wa_strides os, float *ws,
-                         const DecodePlan &plan, hipStream_t stream);
+                         const DecodePlan &plan, hipStream_t stream,
+                         const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr,
+                         wa_strides ns = wa_strides{0, 0, 0});
 
 // ---- encoder / prefill attention ----------------------------------------
 hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
