@@ -200,6 +200,33 @@ class Workload:
         self.decode(i, rec, 3)
 
 
+def encoder_windows(steps, g_seed):
+    """Encoder attention at the 10-s (500 frames, B=144) and 15-s (750
+    frames, B=64) windows: the same B*T^2 work as the 30-s chunk."""
+    import whisper_attention_amd as wa
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    res = {}
+    for name, B, T in (("10s", 144, 500), ("15s", 64, 750)):
+        H = 20
+        q, k, v = (gen_bf16((B, T, H, HEAD_DIM), g) for _ in range(3))
+        o = torch.empty_like(q)
+        for _ in range(3):
+            wa.wa_encoder_attn(q, k, v, out=o, softmax_scale=0.125)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            wa.wa_encoder_attn(q, k, v, out=o, softmax_scale=0.125)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+        tf = 4.0 * B * H * T * T * HEAD_DIM / (us * 1e-6) / 1e12
+        res[name] = {"B": B, "T": T, "us": round(us, 2), "TFLOP/s": round(tf, 2),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o
+    return res
+
+
 def cpu_baseline(budget_s):
     """The CPU oracle on a bounded sample of the encoder workload: whole
     (b, h) pairs of B=16 x H=20 x T=1500 until ``budget_s`` seconds pass."""
@@ -266,6 +293,7 @@ def main():
     torch.cuda.synchronize()
     dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
+    windows = encoder_windows(args.steps, g_seed=1)
     if args.copy_calib:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -324,6 +352,7 @@ def main():
         "kv_quant": {"value": round(quant_gbps, 1), "unit": "GB/s",
                      "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
                      "note": "two calls (K and V), each amax + scale + encode kernels"},
+        "encoder_windows": windows,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "roofline": {"bound": "mfma", "kernel": "encoder_attn_kernel",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

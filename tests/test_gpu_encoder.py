@@ -81,6 +81,21 @@ def test_large_v3_encoder_full_size_sampled(gpu):
     _check(got, q, k, v, None, False, "encoder large-v3 (sampled)", pairs=pairs)
 
 
+@pytest.mark.parametrize("name", ["enc_10s", "enc_15s"])
+def test_shorter_windows_full_size_sampled(gpu, name):
+    """10-s and 15-s chunks (500 and 750 frames) at full batch size."""
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS[name]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    announce(f"encoder {name} B={B} H={H} T={T} (sampled (b, h))")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=0)
+    got = _gpu(wa, q, k, v, None, False)
+    assert torch.isfinite(got.float()).all()
+    g = np.random.default_rng(2)
+    pairs = [(0, 0), (B - 1, H - 1)] + [(int(g.integers(B)), int(g.integers(H))) for _ in range(6)]
+    _check(got, q, k, v, None, False, f"encoder {name} (sampled)", pairs=pairs)
+
+
 def test_prefill_causal_full_size(gpu):
     import whisper_attention_amd as wa
     cfg = workloads.CONFIGS["prefill"]

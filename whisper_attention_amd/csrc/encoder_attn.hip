@@ -4,9 +4,11 @@
 // whisper-blaze 0.1.8 ("Direct Kernel API"), placed in the model as in
 // "Unlocking the power of OpenAI's Whisper", section 3.
 //
-// One block = 8 waves = 512 queries of one (b, h); each wave owns 64 queries
+// One block = 4 waves = 256 queries of one (b, h); each wave owns 64 queries
 // (two 32-query MFMA blocks, so every K and V fragment read from LDS feeds
-// two MFMAs) and walks the keys in tiles of 64.
+// two MFMAs) and walks the keys in tiles of 64.  Two blocks share a CU
+// (one wave of each on every SIMD), so one block's matrix work runs while the
+// other's vector work does.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form, so the
 // accumulator's lane index is the query:
@@ -19,14 +21,12 @@
 // out already in the B-operand order of the second product: P^T is converted
 // to bf16 in place, with no shuffles.
 //
-// Ping-pong between two wave groups.  The 8 waves form two groups of four,
-// one wave of each on every SIMD.  Between two barriers (one "interval" per
-// key tile t) group A runs its matrix work first -- P(t-1).V(t-1) and
-// S(t) = K(t).Q^T -- and then the softmax of S(t) on the vector ALU, while
-// group B does the same work in the other order: the softmax of the S(t-1)
-// it carried over the barrier, then P(t-1).V(t-1) and S(t).  So on each SIMD
-// one wave keeps the matrix cores busy while the other runs exp / convert /
-// sum on the vector ALU, and the barrier keeps the two in that phase.
+// Each interval (one per key tile t) runs the matrix work -- P(t-1).V(t-1)
+// and S(t) = K(t).Q^T -- and then the softmax of tile t on the vector ALU.
+// Eight waves in two groups that alternate those phases under a shared
+// barrier were measured slower than these two independent four-wave blocks
+// per CU, and interleaving a wave's own P(t-1).V(t-1) with its exponentials
+// needs more registers than two waves per SIMD leave.
 //
 // K and V tiles are copied global -> LDS by the asynchronous 16-byte
 // global_load_lds instruction (no register staging) into four stages:
@@ -59,8 +59,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+constexpr int kWaves = 4;
 constexpr int kQW = 64;                   // queries per wave (two 32-query MFMA blocks)
-constexpr int kGroupQueries = 4 * kQW;    // queries of one group of four waves
+constexpr int kBM = kWaves * kQW;         // queries per block
+constexpr int kCopies = 2;                // 8-row copy instructions per wave per K/V tile
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
 constexpr int kStageBytes = 2 * kTileBytes;  // K then V
@@ -140,9 +142,8 @@ __device__ __forceinline__ uint32_t lds_addr(int stage) {
 }
 
 // Issue the asynchronous copy of the K/V tile that starts at row k0 into a
-// stage.  Wave w fills K rows and V rows [8*kCopies*w, 8*kCopies*(w+1)) of
-// the stage, 8 rows per copy instruction.
-template <int kCopies>
+// stage.  Wave w fills K rows and V rows [16w, 16w+16) of the stage, 8 rows
+// per copy instruction.
 __device__ __forceinline__ void issue_tile(int stage, const uint16_t *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
                                            const CopyOffsets (&full)[kCopies], int lane, int w) {
@@ -235,12 +236,14 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][2], const float
   }
 }
 
-// Online softmax of one tile's scores (vector ALU only): mask, tile max,
-// lazy rescale of O and l, P = exp2(S*c - m) as bf16 P^T operands, row sums.
+// Mask and tile max of one tile's scores, and the lazy-rescale decision:
+// the running max moves only when some query's tile max exceeds it by more
+// than kLazy (P then stays below 2^kLazy, which the bf16 weights and fp32
+// sums carry exactly as well).  Returns whether it moved; alpha[qb] is then
+// the factor that takes O and l from the old frame to the new one.
 template <bool kCausal>
-__device__ __forceinline__ void softmax_tile(WaveState &st, f32x16 (&s)[2][2], int k0, int len,
-                                             int wq_lo, float c_log2, int lane,
-                                             bf16x8 (&pb)[2][4]) {
+__device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][2], int k0, int len,
+                                         int wq_lo, float c_log2, int lane, float (&alpha)[2]) {
   const int half = lane >> 5, col = lane & 31;
   if (k0 + kBN > len || (kCausal && k0 + kBN - 1 > wq_lo)) {
 #pragma unroll
@@ -269,32 +272,29 @@ __device__ __forceinline__ void softmax_tile(WaveState &st, f32x16 (&s)[2][2], i
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
     mt[qb] = max_with_lane_xor32(mx) * c_log2;
   }
-  // Lazy rescale: keep the running max unless some query's tile max exceeds
-  // it by more than kLazy (P then stays below 2^kLazy, which the bf16
-  // weights and fp32 sums carry exactly as well).
-  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m_run[0] + kLazy || mt[1] > st.m_run[1] + kLazy) != 0) {
+  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m_run[0] + kLazy || mt[1] > st.m_run[1] + kLazy) == 0)
+    return false;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_new = fmaxf(st.m_run[qb], mt[qb]);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
-      st.oacc[0][qb] *= alpha;
-      st.oacc[1][qb] *= alpha;
-      // row sums: lane n < 16 holds query n in element 0 and query n+16 in
-      // element 1 (see row_sum_selector); the latter's factor is in lane n+16
-      const float alpha_hi = __shfl(alpha, (lane & 15) + 16, 64);
-      st.lacc[qb][0] *= alpha;
-      st.lacc[qb][1] *= alpha_hi;
-      st.m_run[qb] = m_new;
-    }
+  for (int qb = 0; qb < 2; ++qb) {
+    const float m_new = fmaxf(st.m_run[qb], mt[qb]);
+    alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);   // 0 on the first tile
+    st.m_run[qb] = m_new;
   }
-  // The exponentials go to the transcendental unit at a quarter of the FMA
-  // rate; the scheduling groups interleave them with the FMAs and
-  // conversions, which then issue in their shadow instead of before them.
-  softmax_exp(s, st.m_run, c_log2, pb);
+  return true;
+}
+
+// O and the row sums from the old frame to the new one (after a tile max
+// moved the running max).
+__device__ __forceinline__ void rescale(WaveState &st, const float (&alpha)[2], int lane) {
 #pragma unroll
-  for (int g = 0; g < 64; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
+  for (int qb = 0; qb < 2; ++qb) {
+    st.oacc[0][qb] *= alpha[qb];
+    st.oacc[1][qb] *= alpha[qb];
+    // row sums: lane n < 16 holds query n in element 0 and query n+16 in
+    // element 1 (see row_sum_selector); the latter's factor is in lane n+16
+    const float alpha_hi = __shfl(alpha[qb], (lane & 15) + 16, 64);
+    st.lacc[qb][0] *= alpha[qb];
+    st.lacc[qb][1] *= alpha_hi;
   }
 }
 
@@ -340,29 +340,25 @@ __device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
   }
 }
 
-template <int kCopies>
 struct Ctx {
   const uint16_t *kp, *vp;
   wa_strides ks, vs;
   CopyOffsets co[kCopies];
   ReadOffsets ro;
-  int nt, kend, len, wq_lo, lane, w, group;
+  int nt, kend, len, wq_lo, lane, w;
   float c_log2;
 };
 
 // Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+2 is
 // copied into `ahead` (the stage of tile t-2, whose last reads were in
-// interval t-1).  Both groups pass the same barriers, one per interval.
-template <int kCopies>
-__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx<kCopies> &x) {
-  // Keep every instruction of the previous interval above the barrier: the
-  // scheduler would otherwise sink matrix instructions (they touch no memory)
-  // past it and break the two groups' phase alignment.
+// interval t-1).  The block's waves pass one barrier per interval.
+__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx &x) {
+  // Keep every instruction of the previous interval above the barrier.
   __builtin_amdgcn_sched_barrier(0);
   // This wave's copies of tile t are complete -- only tile t+1's 2*kCopies
   // copies may still be in flight -- and so are its LDS reads of interval
-  // t-1 (the immediate holds vmcnt in bits 3:0 and lgkmcnt 0).  Then
-  // a bare barrier (a workgroup fence would wait for tile t+1's copies too):
+  // t-1 (the immediate holds vmcnt in bits 3:0 and lgkmcnt 0).  Then a bare
+  // barrier (a workgroup fence would wait for tile t+1's copies too):
   // afterwards tile t is in LDS for everyone and the stage of tile t-2 is free.
   if (t + 1 < x.nt)
     __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0 + 2 * kCopies);
@@ -372,53 +368,44 @@ __device__ __forceinline__ void open_interval(int ahead, int t, const Ctx<kCopie
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if (t + 2 < x.nt)
-    issue_tile<kCopies>(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
+  if (t + 2 < x.nt) issue_tile(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
-template <bool kCausal, int kCopies>
-__device__ __forceinline__ bool wave_needs(int j, const Ctx<kCopies> &x) {
+template <bool kCausal>
+__device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
   return j >= 0 && j < x.nt && !(kCausal && j * kBN > x.wq_lo + kQW - 1);
 }
 
-// Group A: P(t-1).V(t-1) and S(t) on the matrix cores, then softmax(t);
-// P(t) is carried to the next interval.
-template <bool kCausal, int kCopies>
-__device__ __forceinline__ void interval_a(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
-                                           const uint8_t *prev, int ahead, int t,
-                                           const Ctx<kCopies> &x) {
+// Interval t: P(t-1).V(t-1) and S(t) on the matrix cores, then the softmax
+// of tile t on the vector ALU (the other block on the CU fills the matrix
+// cores meanwhile).  P(t) is carried to the next interval in `pa`.
+template <bool kCausal>
+__device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
+                                         const uint8_t *prev, int ahead, int t, const Ctx &x) {
   open_interval(ahead, t, x);
-  if (wave_needs<kCausal, kCopies>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
-  if (wave_needs<kCausal, kCopies>(t, x)) {
+  if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
+  if (wave_needs<kCausal>(t, x)) {
     f32x16 s[2][2];
     scores(st, cur, x.ro, s);
     __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
-    softmax_tile<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, pa);
+    float alpha[2];
+    if (tile_max<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, alpha))
+      rescale(st, alpha, x.lane);
+    // The exponentials go to the transcendental unit at a quarter of the FMA
+    // rate; the scheduling groups interleave them with the FMAs and
+    // conversions, which then issue in their shadow instead of before them.
+    softmax_exp(s, st.m_run, x.c_log2, pa);
+#pragma unroll
+    for (int g = 0; g < 64; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
+    }
   }
 }
 
-// Group B: softmax(t-1) of the carried S(t-1) first, then P(t-1).V(t-1) and
-// S(t) on the matrix cores; S(t) is carried to the next interval.
-template <bool kCausal, int kCopies>
-__device__ __forceinline__ void interval_b(WaveState &st, f32x16 (&sb)[2][2], const uint8_t *cur,
-                                           const uint8_t *prev, int ahead, int t,
-                                           const Ctx<kCopies> &x) {
-  open_interval(ahead, t, x);
-  if (wave_needs<kCausal, kCopies>(t - 1, x)) {
-    bf16x8 pb[2][4];
-    softmax_tile<kCausal>(st, sb, (t - 1) * kBN, x.len, x.wq_lo, x.c_log2, x.lane, pb);
-    __builtin_amdgcn_sched_barrier(0);  // vector phase, then matrix phase
-    accumulate_pv(st, prev + kTileBytes, x.ro, pb);
-  }
-  if (wave_needs<kCausal, kCopies>(t, x)) scores(st, cur, x.ro, sb);
-}
-
-// kGroups = 2: eight waves in two ping-pong groups, 512 queries per block.
-// kGroups = 1: group A alone, four waves and 256 queries per block (short
-// sequences: two such blocks share a CU and interleave on their own).
-template <bool kCausal, int kGroups>
-__global__ __launch_bounds__(kGroups * 256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
+template <bool kCausal>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
     const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
@@ -433,15 +420,12 @@ __global__ __launch_bounds__(kGroups * 256) __attribute__((amdgpu_waves_per_eu(2
   if (kCausal) qt = n_qt - 1 - qt;  // longest rows first
   const int b = bh / H, h = bh - b * H;
   const int len = min(max(lens ? lens[b] : T_max, 0), T_max);
-  constexpr int kBM = kGroups * kGroupQueries;
-  constexpr int kCopies = 2 / kGroups;   // 8-row copy instructions per wave per K/V tile
   const int q0 = qt * kBM;
   if (q0 >= len) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int group = w >> 2;
-  Ctx<kCopies> x;
+  Ctx x;
   x.kp = k + (long)b * ks.b + (long)h * ks.h;
   x.vp = v + (long)b * vs.b + (long)h * vs.h;
   x.ks = ks;
@@ -449,16 +433,14 @@ __global__ __launch_bounds__(kGroups * 256) __attribute__((amdgpu_waves_per_eu(2
   x.kend = kCausal ? min(len, q0 + kBM) : len;
   x.nt = (x.kend + kBN - 1) / kBN;
   x.len = len;
-  // group A holds queries [q0, q0+256), group B [q0+256, q0+512)
-  x.wq_lo = q0 + group * kGroupQueries + (w & 3) * kQW;
+  x.wq_lo = q0 + w * kQW;
   x.lane = lane;
   x.w = w;
-  x.group = group;
   x.c_log2 = c_log2;
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopies + i) * 8);
-  issue_tile<kCopies>(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
-  if (x.nt > 1) issue_tile<kCopies>(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
+  issue_tile(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
+  if (x.nt > 1) issue_tile(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
   x.ro = read_offsets(lane);
 
   WaveState st;
@@ -482,30 +464,16 @@ __global__ __launch_bounds__(kGroups * 256) __attribute__((amdgpu_waves_per_eu(2
                "v"(st.qreg[1][0]), "v"(st.qreg[1][1]), "v"(st.qreg[1][2]), "v"(st.qreg[1][3]));
 
   // intervals t = 0 .. nt: tile t's K and tile t-1's V; the stage of tile j
-  // is j % 4.  Each group runs its own loop (its carried operands stay in
-  // registers); both pass one barrier per interval.
-  if (kGroups == 1 || group == 0) {
-    bf16x8 pa[2][4];
-    for (int t = 0; t <= x.nt; t += 4) {
-      interval_a<kCausal, kCopies>(st, pa, g_lds[0], g_lds[3], 2, t, x);
-      if (t + 1 > x.nt) break;
-      interval_a<kCausal, kCopies>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
-      if (t + 2 > x.nt) break;
-      interval_a<kCausal, kCopies>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
-      if (t + 3 > x.nt) break;
-      interval_a<kCausal, kCopies>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
-    }
-  } else {
-    f32x16 sb[2][2];
-    for (int t = 0; t <= x.nt; t += 4) {
-      interval_b<kCausal, kCopies>(st, sb, g_lds[0], g_lds[3], 2, t, x);
-      if (t + 1 > x.nt) break;
-      interval_b<kCausal, kCopies>(st, sb, g_lds[1], g_lds[0], 3, t + 1, x);
-      if (t + 2 > x.nt) break;
-      interval_b<kCausal, kCopies>(st, sb, g_lds[2], g_lds[1], 0, t + 2, x);
-      if (t + 3 > x.nt) break;
-      interval_b<kCausal, kCopies>(st, sb, g_lds[3], g_lds[2], 1, t + 3, x);
-    }
+  // is j % 4.
+  bf16x8 pa[2][4];
+  for (int t = 0; t <= x.nt; t += 4) {
+    interval<kCausal>(st, pa, g_lds[0], g_lds[3], 2, t, x);
+    if (t + 1 > x.nt) break;
+    interval<kCausal>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
+    if (t + 2 > x.nt) break;
+    interval<kCausal>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
+    if (t + 3 > x.nt) break;
+    interval<kCausal>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
   }
 
 #pragma unroll
@@ -540,26 +508,15 @@ hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, w
                           int H, int T_max, const int32_t *lens, int causal,
                           float softmax_scale, hipStream_t stream) {
   const float c_log2 = softmax_scale * kLog2e;
-  // short sequences (a decoder prompt) fit one four-wave group
-  const int groups = T_max <= kGroupQueries ? 1 : 2;
-  const int n_qt = (T_max + groups * kGroupQueries - 1) / (groups * kGroupQueries);
+  const int n_qt = (T_max + kBM - 1) / kBM;
   const long total = (long)B * H * n_qt;
-  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(groups * 256);
-  if (causal) {
-    if (groups == 1)
-      hipLaunchKernelGGL((attn_fwd_kernel<true, 1>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
-                         os, H, T_max, lens, c_log2, n_qt, (int)total);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<true, 2>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
-                         os, H, T_max, lens, c_log2, n_qt, (int)total);
-  } else {
-    if (groups == 1)
-      hipLaunchKernelGGL((attn_fwd_kernel<false, 1>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
-                         os, H, T_max, lens, c_log2, n_qt, (int)total);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<false, 2>), grid, block, 0, stream, q, qs, k, ks, v, vs, o,
-                         os, H, T_max, lens, c_log2, n_qt, (int)total);
-  }
+  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(kWaves * 64);
+  if (causal)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H,
+                       T_max, lens, c_log2, n_qt, (int)total);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H,
+                       T_max, lens, c_log2, n_qt, (int)total);
   return hipGetLastError();
 }
 

@@ -113,6 +113,10 @@ CONFIGS = {
     # decoder prompt prefill + cache fill: lengths U[4,224], 1% outliers x20
     "prefill": dict(B=128, H=20, T=224, lo=4, hi=224, outlier_p=0.01, outlier_mult=20.0,
                     gran="head"),
+    # encoder at the shorter windows: 10-s (500 frames) and 15-s (750
+    # frames) chunks, batches sized to the same B*T^2 work as enc_l3
+    "enc_10s": dict(B=144, H=20, T=500),
+    "enc_15s": dict(B=64, H=20, T=750),
     # long audio: 256 chunks (thirty per 15-minute file), Zipf(1.2) self
     # lengths capped at 448, per-head scales
     "long": dict(B=256, H=20, cross_len=ENC_FRAMES, zipf_a=1.2, cap=DEC_MAX_TOKENS,
