@@ -200,6 +200,51 @@ class Workload:
         self.decode(i, rec, 3)
 
 
+def decode_step_graph(wl, layers=32, iters=10):
+    """A Whisper large-v3 decode step over its 32 decoder layers: per layer
+    the self-attention step with its append, then the cross-attention (cache
+    set l % N_SETS for layer l), launched eagerly and as one HIP graph."""
+    wa = wl.wa
+
+    def step():
+        for layer in range(layers):
+            c = wl.sets[layer % N_SETS]
+            (sk, sks), (sv, svs) = c["sk"], c["sv"]
+            (xk, xks), (xv, xvs) = c["xk"], c["xv"]
+            wa.wa_decode_attn_append(wl.qd, wl.kn, wl.vn, sk, sv, sks, svs, wl.lens_s, "tensor", 0.125,
+                                     out=wl.od_a, workspace=wl.ws_ds)
+            wa.wa_decode_attn(wl.od_a, xk, xv, xks, xvs, wl.lens_x, "tensor", 0.125, out=wl.od_x,
+                              workspace=wl.ws_dx)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for _ in range(iters):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / iters, (time.perf_counter() - t0) * 1e6 / iters
+
+    eager_gpu, eager_wall = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph_gpu, graph_wall = timed(graph.replay)
+    return {"layers": layers, "B": wl.dec["B"], "eager_us": round(eager_wall, 1),
+            "graph_us": round(graph_wall, 1), "eager_gpu_us": round(eager_gpu, 1),
+            "graph_gpu_us": round(graph_gpu, 1),
+            "note": "per decode step, wall clock per step over the loop (host launch cost included)"}
+
+
 def encoder_windows(steps, g_seed):
     """Encoder attention at the 10-s (500 frames, B=144) and 15-s (750
     frames, B=64) windows: the same B*T^2 work as the 30-s chunk."""
@@ -294,6 +339,7 @@ def main():
     dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
     windows = encoder_windows(args.steps, g_seed=1)
+    graph_step = decode_step_graph(wl)
     if args.copy_calib:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -353,6 +399,7 @@ def main():
                      "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
                      "note": "two calls (K and V), each amax + scale + encode kernels"},
         "encoder_windows": windows,
+        "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "roofline": {"bound": "mfma", "kernel": "encoder_attn_kernel",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
