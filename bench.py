@@ -43,8 +43,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # counts are in profiles/hbm_traffic_counters.md), with the sha256 prefix of
 # the kernel source they were taken on: a changed kernel reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("db7713cc13134171", {"encoder": 252.4e6, "prefill": 148.5e6}),
-    "decode_attn.hip": ("85c22582c6bb3570", {"cross": 246.2e6, "self": 42.1e6}),
+    "encoder_attn.hip": ("04de279e6fbed296", {"encoder": 251.98e6, "prefill": 148.25e6}),
+    "decode_attn.hip": ("05856125f2689f36", {"cross": 246.21e6, "self": 42.13e6}),
 }
 
 
@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="leave out the captured-graph decode step (for counter collection runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -200,21 +202,59 @@ class Workload:
         self.decode(i, rec, 3)
 
 
-def decode_step_graph(wl, layers=32, iters=10):
-    """A Whisper large-v3 decode step over its 32 decoder layers: per layer
-    the self-attention step with its append, then the cross-attention (cache
-    set l % N_SETS for layer l), launched eagerly and as one HIP graph."""
-    wa = wl.wa
+class DecodeLayers:
+    """Inputs of a decode step over the decoder's layers: per layer a cross
+    cache of Lx frames and a self cache of lengths U[1, Ls], E4M3 per-tensor,
+    filled by the quantize kernel. ``sets`` (with the self lengths
+    ``lens_s`` they were filled with) reuses given cache sets in turn instead
+    of filling new ones."""
+
+    def __init__(self, wa, B, H, Lx, Ls, layers, g, seed, sets=None, lens_s=None):
+        dev = "cuda"
+        self.B, self.layers = B, layers
+        if lens_s is None:
+            import workloads
+            lens_s = torch.from_numpy(workloads.lens_uniform(B, 1, Ls, seed)).to(dev)
+        self.lens_s = lens_s
+        self.lens_x = torch.full((B,), Lx, dtype=torch.int32, device=dev)
+        self.q = gen_bf16((B, H, HEAD_DIM), g)
+        self.kn = gen_bf16((B, H, HEAD_DIM), g)
+        self.vn = gen_bf16((B, H, HEAD_DIM), g)
+        self.o_self = torch.empty_like(self.q)
+        self.o_cross = torch.empty_like(self.q)
+        if sets is None:
+            sets = []
+            for _ in range(layers):
+                caches = {}
+                for name, L, lens in (("x", Lx, None), ("s", Ls, self.lens_s)):
+                    for kv in ("k", "v"):
+                        src = gen_bf16((B, L, H, HEAD_DIM), g)
+                        c = torch.zeros((B, H, L, HEAD_DIM), dtype=torch.uint8, device=dev)
+                        sc = torch.zeros(1, dtype=torch.float32, device=dev)
+                        wa.wa_kv_quant_fp8(src, c, sc, "tensor", lens=lens)
+                        caches[name + kv] = (c, sc)
+                sets.append(caches)
+        self.sets = sets
+        self.ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8,
+                                device=dev)
+        self.ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8,
+                                device=dev)
+
+
+def decode_step_graph(wa, d, iters=10):
+    """A decode step over the decoder's layers: per layer the self-attention
+    step with its append, then the cross-attention on the self output, launched
+    eagerly and as one HIP graph."""
 
     def step():
-        for layer in range(layers):
-            c = wl.sets[layer % N_SETS]
+        for layer in range(d.layers):
+            c = d.sets[layer % len(d.sets)]
             (sk, sks), (sv, svs) = c["sk"], c["sv"]
             (xk, xks), (xv, xvs) = c["xk"], c["xv"]
-            wa.wa_decode_attn_append(wl.qd, wl.kn, wl.vn, sk, sv, sks, svs, wl.lens_s, "tensor", 0.125,
-                                     out=wl.od_a, workspace=wl.ws_ds)
-            wa.wa_decode_attn(wl.od_a, xk, xv, xks, xvs, wl.lens_x, "tensor", 0.125, out=wl.od_x,
-                              workspace=wl.ws_dx)
+            wa.wa_decode_attn_append(d.q, d.kn, d.vn, sk, sv, sks, svs, d.lens_s, "tensor", 0.125,
+                                     out=d.o_self, workspace=d.ws_s)
+            wa.wa_decode_attn(d.o_self, xk, xv, xks, xvs, d.lens_x, "tensor", 0.125, out=d.o_cross,
+                              workspace=d.ws_x)
 
     def timed(fn):
         fn()
@@ -239,10 +279,23 @@ def decode_step_graph(wl, layers=32, iters=10):
     with torch.cuda.graph(graph):
         step()
     graph_gpu, graph_wall = timed(graph.replay)
-    return {"layers": layers, "B": wl.dec["B"], "eager_us": round(eager_wall, 1),
-            "graph_us": round(graph_wall, 1), "eager_gpu_us": round(eager_gpu, 1),
-            "graph_gpu_us": round(graph_gpu, 1),
-            "note": "per decode step, wall clock per step over the loop (host launch cost included)"}
+    return {"layers": d.layers, "B": d.B, "eager_us": round(eager_wall, 1), "graph_us": round(graph_wall, 1),
+            "eager_gpu_us": round(eager_gpu, 1), "graph_gpu_us": round(graph_gpu, 1)}
+
+
+def decode_steps_graph(wl, g_seed):
+    """32-layer decode step at the bench batch (the bench's cache sets in
+    turn) and at batch 1 (a cache per layer), eager and captured."""
+    wa, dec = wl.wa, wl.dec
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    big = DecodeLayers(wa, dec["B"], dec["H"], dec["Lx"], dec["Ls"], 32, g, g_seed, sets=wl.sets,
+                       lens_s=wl.lens_s)
+    one = DecodeLayers(wa, 1, dec["H"], dec["Lx"], dec["Ls"], 32, g, g_seed)
+    torch.cuda.synchronize()
+    return {"B64": decode_step_graph(wa, big), "B1": decode_step_graph(wa, one),
+            "note": "microseconds per 32-layer decode step (append + self, then cross, per layer): wall "
+                    "clock per step over the loop (host launch cost included) and GPU event time"}
 
 
 def encoder_windows(steps, g_seed):
@@ -339,7 +392,7 @@ def main():
     dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
     windows = encoder_windows(args.steps, g_seed=1)
-    graph_step = decode_step_graph(wl)
+    graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
     if args.copy_calib:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -401,7 +454,7 @@ def main():
         "encoder_windows": windows,
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
-        "roofline": {"bound": "mfma", "kernel": "encoder_attn_kernel",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false> (encoder)",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic("encoder_attn.hip", "encoder"), "traffic_unit": "bytes per launch",
