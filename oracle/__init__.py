@@ -15,12 +15,16 @@ What it computes, and where the pages define it:
   "Direct Kernel API": ``quantise_e4m3``); the HF blog post "Blazingly fast
   whisper transcriptions with Inference Endpoints" (section "Inference
   Stack") fixes that the KV cache is stored in one-byte float8.
+* ``e5m2``  -- the OCP float8 E5M2 codec, the second FP8 format that
+  whisper-blaze's feature list names: exact decode of all 256 codes and a
+  round-to-nearest-even encode that saturates at 57344.
 * ``quant`` -- dynamic KV quantization: abs-max per scale group, the
-  dequantization multiplier ``scale = amax / 448`` and the codes
-  ``E4M3(x / scale)``; whisper-blaze "Direct Kernel API" (quantise returns
-  codes plus a scale; dequantise takes codes and that scale) and its
-  feature list ("per-tensor scaling"); HF blog "Inference Stack"
-  ("dynamically quantizing activations" for the KV cache).
+  dequantization multiplier ``scale = amax / 448`` (E4M3; 57344 for E5M2)
+  and the codes ``FMT(x / scale)``, and the dequantise back to bf16;
+  whisper-blaze "Direct Kernel API" (quantise returns codes plus a scale;
+  dequantise takes codes and that scale) and its feature list ("per-tensor
+  scaling"); HF blog "Inference Stack" ("dynamically quantizing
+  activations" for the KV cache).
 * ``attn``  -- softmax attention: dense non-causal (encoder
   self-attention), causal and ragged (decoder prompt prefill), and one
   query token against an fp8 cache (decoder self- and cross-attention),
