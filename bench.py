@@ -298,6 +298,47 @@ def decode_steps_graph(wl, g_seed):
                     "clock per step over the loop (host launch cost included) and GPU event time"}
 
 
+def codec_rates(wl, steps):
+    """The float8 codec calls on the bench's caches: dequantise of the decode
+    cross K cache (B=64 H=20 L=1500, E4M3, per tensor) to bf16, and the E5M2
+    quantize of the prefill K and V (per head, dynamic scales)."""
+    wa = wl.wa
+    xk, xks = wl.sets[0]["xk"]
+    B, H, L = xk.shape[0], xk.shape[1], xk.shape[2]
+    out = torch.empty((B, L, H, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    kc5, vc5 = torch.zeros_like(wl.kcp), torch.zeros_like(wl.vcp)
+    ks5, vs5 = torch.zeros_like(wl.ksp), torch.zeros_like(wl.vsp)
+
+    def dq(i):
+        c, sc = wl.sets[i % N_SETS]["xk"]
+        wa.wa_kv_dequant_fp8(c, sc, "tensor", "e4m3", out=out)
+
+    def q5(i):
+        wa.wa_kv_quant_fp8_fmt(wl.kp, kc5, ks5, "head", "e5m2", lens=wl.lens_p, workspace=wl.ws_q)
+        wa.wa_kv_quant_fp8_fmt(wl.vp, vc5, vs5, "head", "e5m2", lens=wl.lens_p, workspace=wl.ws_q)
+
+    res = {}
+    for name, fn in (("dequant", dq), ("quant_e5m2", q5)):
+        for i in range(3):
+            fn(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        res[name] = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    dq_bytes = 3.0 * B * H * L * HEAD_DIM          # 1 code byte read, 2 bf16 bytes written
+    return {"kv_dequant": {"value": round(dq_bytes / (res["dequant"] * 1e-6) / 1e9, 1), "unit": "GB/s",
+                           "frac": round(dq_bytes / (res["dequant"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                           "us": round(res["dequant"], 2),
+                           "note": f"E4M3 cache B={B} H={H} L={L} -> bf16, the {N_SETS} cache sets in turn"},
+            "kv_quant_e5m2": {"value": round(wl.quant_bytes() / (res["quant_e5m2"] * 1e-6) / 1e9, 1),
+                              "unit": "GB/s", "us": round(res["quant_e5m2"], 2),
+                              "note": "prefill K and V to E5M2, per-head dynamic scales (as kv_quant)"}}
+
+
 def encoder_windows(steps, g_seed):
     """Encoder attention at the 10-s (500 frames, B=144) and 15-s (750
     frames, B=64) windows: the same B*T^2 work as the 30-s chunk."""
@@ -393,6 +434,7 @@ def main():
     dms = dseg.mean(axis=0)
     windows = encoder_windows(args.steps, g_seed=1)
     graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
+    codecs = codec_rates(wl, args.steps)
     if args.copy_calib:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -451,6 +493,7 @@ def main():
         "kv_quant": {"value": round(quant_gbps, 1), "unit": "GB/s",
                      "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
                      "note": "two calls (K and V), each amax + scale + encode kernels"},
+        **codecs,
         "encoder_windows": windows,
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},

@@ -1,13 +1,17 @@
 /*
  * wa.h -- C ABI of the Whisper attention hot path on MI355X (gfx950).
  *
- * Three operations, all asynchronous on the caller's HIP stream:
+ * Operations, all asynchronous on the caller's HIP stream:
  *
  *   wa_kv_quant_fp8  bf16 -> float8 E4M3 quantization that fills a KV cache
+ *                    (wa_kv_quant_fp8_fmt: E4M3 or E5M2)
+ *   wa_kv_dequant_fp8  float8 cache -> bf16, the inverse read
  *   wa_encoder_attn  dense bf16 softmax attention (encoder self-attention,
  *                    or causal decoder prompt prefill), ragged by length
  *   wa_decode_attn   one query token per sequence against an E4M3 KV cache
  *                    (decoder self-attention or cross-attention)
+ *   wa_decode_attn_append  the same for decoder self-attention, with the
+ *                    step's token written into the cache in the same launch
  *
  * Sources for what is computed:
  *   - "Blazingly fast whisper transcriptions with Inference Endpoints" (HF
@@ -67,6 +71,11 @@ typedef enum {
   WA_SCALE_PER_HEAD = 1          /* one scale per head: scale[H] */
 } wa_scale_gran;
 
+typedef enum {
+  WA_FP8_E4M3 = 0,               /* OCP E4M3: bias 7, max 448, NaN only */
+  WA_FP8_E5M2 = 1                /* OCP E5M2: bias 15, max 57344, +-inf and NaN */
+} wa_fp8_format;
+
 /* Element strides of the batch, position and head axes. */
 typedef struct {
   int64_t b, t, h;
@@ -107,6 +116,52 @@ wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_
                           size_t workspace_bytes, hipStream_t stream);
 
 size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gran);
+
+/*
+ * wa_kv_quant_fp8_fmt -- wa_kv_quant_fp8 with the float8 format chosen.
+ *
+ * What: whisper-blaze 0.1.8 (PyPI page, feature list) names both OCP float8
+ *   formats, E4M3 and E5M2.  fmt = WA_FP8_E4M3 is exactly wa_kv_quant_fp8.
+ *   fmt = WA_FP8_E5M2 replaces 448 by E5M2's largest finite value 57344:
+ *     scale[g] = fp32(amax_g / 57344)   (1 when amax_g is 0),
+ *     code = E5M2(clamp(fp32(x / scale[g]), -57344, 57344))
+ *   rounded to nearest even; codes are never +-inf or NaN.  Arguments,
+ *   workspace and errors are those of wa_kv_quant_fp8; a bad fmt is
+ *   WA_ERR_INVALID_ARGUMENT.
+ */
+wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                              int head_dim, const int32_t *lens, const int32_t *dst_start,
+                              uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                              wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * wa_kv_dequant_fp8 -- read a float8 KV cache back as bf16.
+ *
+ * What: the dequantise of whisper-blaze 0.1.8 ("Direct Kernel API":
+ *   dequantise_e4m3 takes the codes and the scale quantise_e4m3 returned;
+ *   feature list: "FP8 quantize/dequantize with per-tensor scaling").  For
+ *   every sequence b, head h and position t < n, n = lens[b] clamped to
+ *   [0, min(T_max, cache_len)] (lens NULL: n = min(T_max, cache_len)):
+ *     x[b][t][h][:] = bf16(fp32(decode(cache[b][h][t][:]) * scale[g]))
+ *   with decode exact in fp32, the IEEE fp32 product, and the store rounded
+ *   to nearest even.  Positions t >= n of x are not written.  Codes that
+ *   decode to +-inf or NaN (never written by the quantize calls) give +-inf
+ *   or a NaN.
+ *
+ * cache      device uint8 [B][H][cache_len][64] with strides cs (t = slot).
+ * scale      device float32 [1] or [H] (gran).
+ * lens       device int32 [B] or NULL.
+ * x          device bf16 [B][T_max][H][64] with strides xs; must not overlap
+ *            the cache.
+ * Errors: null pointer, non-positive size or bad enum ->
+ *   WA_ERR_INVALID_ARGUMENT; head_dim != 64, B or H above 65535, layout
+ *   (alignment, strides) -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_kv_dequant_fp8(const uint8_t *cache, wa_strides cs, int cache_len,
+                            const float *scale, wa_scale_gran gran, wa_fp8_format fmt,
+                            const int32_t *lens, int B, int H, int T_max, int head_dim,
+                            uint16_t *x, wa_strides xs, hipStream_t stream);
 
 /*
  * wa_encoder_attn -- dense softmax attention over bf16 Q/K/V.

@@ -1,18 +1,21 @@
-/* CPU check of the quotient method of the E4M3 encode kernel.
+/* CPU check of the quotient method of the float8 encode kernels.
  *
- * The kernel computes x / s as q0 = |x| * r, e = |x| - q0 * s (one fused
- * multiply-add), q = min(q0 + e * r, 448) (one fused multiply-add) with the
+ * The kernels compute x / s as q0 = |x| * r, e = |x| - q0 * s (one fused
+ * multiply-add), q = min(q0 + e * r, FMAX) (one fused multiply-add) with the
  * sign of x restored, where r = 1 / s is itself an IEEE division; q0 is first
- * clamped to 449 so no step overflows.  Restated here in C (fmaf is the
- * correctly rounded fused multiply-add) and compared with the IEEE quotient
- * clamped to +-448, for every finite bf16 x.  A pair may differ only where
- * both values are below 2^-12 in magnitude with the same sign: every such
- * value encodes to a zero E4M3 code of that sign, so the codes agree.
+ * clamped to FMAX + 1 so no step overflows.  FMAX is 448 for E4M3 and 57344
+ * for E5M2.  Restated here in C (fmaf is the correctly rounded fused
+ * multiply-add) and compared with the IEEE quotient clamped to +-FMAX, for
+ * every finite bf16 x.  A pair may differ only where both values are at most
+ * half the format's smallest subnormal in magnitude (2^-10 for E4M3, 2^-17
+ * for E5M2) with the same sign: every such value encodes to a zero code of
+ * that sign (a tie at that point rounds to the even code, zero), so the codes
+ * agree.
  *
- * usage: quotient_check STRIDE   -- every STRIDE-th dynamic scale amax/448
- *                                   over the positive finite bf16 amax, plus
- *                                   fixed edge scales; exit status 1 on a
- *                                   mismatch that could change a code.
+ * usage: quotient_check STRIDE [e5m2]
+ *          every STRIDE-th dynamic scale amax/FMAX over the positive finite
+ *          bf16 amax, plus fixed edge scales; exit status 1 on a mismatch
+ *          that could change a code.
  */
 #include <math.h>
 #include <stdint.h>
@@ -23,13 +26,15 @@
 static float from_bits(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
 static uint32_t to_bits(float x) { uint32_t v; memcpy(&v, &x, 4); return v; }
 
-static float ieee(float x, float s) { return fminf(fmaxf(x / s, -448.f), 448.f); }
+static float FMAX = 448.f, ZERO_BELOW = 0x1p-10f;
+
+static float ieee(float x, float s) { return fminf(fmaxf(x / s, -FMAX), FMAX); }
 
 static float method(float x, float s, float r) {
   const float a = fabsf(x);
-  const float q0 = fminf(a * r, 449.f);
+  const float q0 = fminf(a * r, FMAX + 1.f);
   const float e = fmaf(-q0, s, a);
-  const float q = fminf(fmaf(e, r, q0), 448.f);
+  const float q = fminf(fmaf(e, r, q0), FMAX);
   return copysignf(q, x);
 }
 
@@ -41,7 +46,7 @@ static long check(float s) {
     if (!isfinite(x)) continue;
     const float w = ieee(x, s), g = method(x, s, r);
     if (to_bits(w) == to_bits(g)) continue;
-    if (fabsf(w) < 0x1p-12f && fabsf(g) < 0x1p-12f && signbit(w) == signbit(g)) continue;
+    if (fabsf(w) <= ZERO_BELOW && fabsf(g) <= ZERO_BELOW && signbit(w) == signbit(g)) continue;
     if (bad < 3) printf("mismatch: s=%a x=%a ieee=%a method=%a\n", s, x, w, g);
     ++bad;
   }
@@ -50,16 +55,20 @@ static long check(float s) {
 
 int main(int argc, char **argv) {
   const int stride = argc > 1 ? atoi(argv[1]) : 1;
+  if (argc > 2 && strcmp(argv[2], "e5m2") == 0) {
+    FMAX = 57344.f;
+    ZERO_BELOW = 0x1p-17f;
+  }
   long bad = 0, n = 0;
   for (uint32_t b = 1; b < 0x7f80; b += (uint32_t)stride) {   /* dynamic scales */
-    const float s = from_bits(b << 16) / 448.0f;
+    const float s = from_bits(b << 16) / FMAX;
     if (!(s >= 0x1p-80f && s <= 0x1p80f)) continue;
     bad += check(s);
     ++n;
   }
   const float edge[] = {0x1p-80f, 0x1p80f, 0x1.fffffep79f, 0x1.000002p-80f, 1.0f, 0.125f,
-                        1.0f / 448, 4.25f / 448, 93.0f / 448, 0x1.555556p-22f, 0x1.fffffep-1f,
-                        0x1.000002p0f, 3.0f, 0x1.7ffffep5f};
+                        1.0f / 448, 4.25f / 448, 93.0f / 448, 1.0f / 57344, 93.0f / 57344,
+                        0x1.555556p-22f, 0x1.fffffep-1f, 0x1.000002p0f, 3.0f, 0x1.7ffffep5f};
   for (size_t i = 0; i < sizeof edge / sizeof edge[0]; ++i) {
     bad += check(edge[i]);
     ++n;

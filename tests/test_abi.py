@@ -87,6 +87,48 @@ def test_quant_validation(wa):
     assert _quant(wa, wsb=16) == wa.WA_ERR_WORKSPACE_TOO_SMALL
 
 
+def _quant_fmt(wa, fmt, **kw):
+    a = dict(x=FAKE, xs=_S(wa), B=2, H=20, T=1500, D=64, lens=None, dst=None, cache=FAKE,
+             cs=wa.Strides(20 * 1500 * 64, 64, 1500 * 64), L=1500, scale=FAKE, gran=0, cs_=1,
+             ws=FAKE, wsb=0)
+    a.update(kw)
+    return wa.lib.wa_kv_quant_fp8_fmt(a["x"], a["xs"], a["B"], a["H"], a["T"], a["D"], a["lens"],
+                                      a["dst"], a["cache"], a["cs"], a["L"], a["scale"], a["gran"],
+                                      fmt, a["cs_"], a["ws"], a["wsb"], None)
+
+
+def test_quant_fmt_validation(wa):
+    assert _quant_fmt(wa, 2) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _quant_fmt(wa, -1) == wa.WA_ERR_INVALID_ARGUMENT
+    for fmt in (wa.WA_FP8_E4M3, wa.WA_FP8_E5M2):
+        assert _quant_fmt(wa, fmt, x=None) == wa.WA_ERR_INVALID_ARGUMENT
+        assert _quant_fmt(wa, fmt, D=128) == wa.WA_ERR_UNSUPPORTED
+        assert _quant_fmt(wa, fmt, wsb=16) == wa.WA_ERR_WORKSPACE_TOO_SMALL
+
+
+def _dequant(wa, **kw):
+    a = dict(cache=FAKE, cs=wa.Strides(20 * 1500 * 64, 64, 1500 * 64), L=1500, scale=FAKE, gran=0,
+             fmt=0, lens=None, B=2, H=20, T=1500, D=64, x=FAKE, xs=_S(wa))
+    a.update(kw)
+    return wa.lib.wa_kv_dequant_fp8(a["cache"], a["cs"], a["L"], a["scale"], a["gran"], a["fmt"],
+                                    a["lens"], a["B"], a["H"], a["T"], a["D"], a["x"], a["xs"], None)
+
+
+def test_dequant_validation(wa):
+    for name in ("cache", "scale", "x"):
+        assert _dequant(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    for name in ("B", "H", "T", "L"):
+        assert _dequant(wa, **{name: 0}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dequant(wa, gran=2) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dequant(wa, fmt=3) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _dequant(wa, D=32) == wa.WA_ERR_UNSUPPORTED
+    assert _dequant(wa, B=65536) == wa.WA_ERR_UNSUPPORTED
+    assert _dequant(wa, x=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _dequant(wa, cache=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert _dequant(wa, xs=_S(wa, t=20 * 64 + 4)) == wa.WA_ERR_UNSUPPORTED
+    assert _dequant(wa, cs=wa.Strides(20 * 1500 * 64, 8, 1500 * 64)) == wa.WA_ERR_UNSUPPORTED
+
+
 def _enc(wa, **kw):
     s = _S(wa)
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, qs=s, ks=s, vs=s, os=s, B=2, H=20, T=1500, D=64,

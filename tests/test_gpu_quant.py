@@ -20,7 +20,7 @@ def _all_finite_bf16():
     return f
 
 
-def _run_quant(wa, x_cpu, lens, dst, L, gran, scale_in=None, x_dev=None):
+def _run_quant(wa, x_cpu, lens, dst, L, gran, scale_in=None, x_dev=None, fmt="e4m3"):
     """x_cpu: bf16 [B][T][H][64].  Returns (cache uint8 [B][H][L][64], scale float32)."""
     B, T, H, D = x_cpu.shape
     x = x_dev if x_dev is not None else to_dev(x_cpu)
@@ -30,26 +30,31 @@ def _run_quant(wa, x_cpu, lens, dst, L, gran, scale_in=None, x_dev=None):
         scale = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
     else:
         scale = to_dev(np.asarray(scale_in, dtype=np.float32))
-    wa.wa_kv_quant_fp8(x, cache, scale, gran,
-                       lens=None if lens is None else to_dev(np.asarray(lens, dtype=np.int32)),
-                       dst_start=None if dst is None else to_dev(np.asarray(dst, dtype=np.int32)),
-                       compute_scale=scale_in is None)
+    lens_d = None if lens is None else to_dev(np.asarray(lens, dtype=np.int32))
+    dst_d = None if dst is None else to_dev(np.asarray(dst, dtype=np.int32))
+    if fmt == "e4m3":      # the E4M3 entry point itself
+        wa.wa_kv_quant_fp8(x, cache, scale, gran, lens=lens_d, dst_start=dst_d,
+                           compute_scale=scale_in is None)
+    else:
+        wa.wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=lens_d, dst_start=dst_d,
+                               compute_scale=scale_in is None)
     torch.cuda.synchronize()
     return cache.cpu().numpy(), scale.cpu().numpy()
 
 
-def _oracle(x_cpu, lens, dst, L, gran, scale_in=None):
+def _oracle(x_cpu, lens, dst, L, gran, scale_in=None, fmt="e4m3"):
     x = x_cpu.float().numpy()
     B, T, H, D = x.shape
     lens = np.full(B, T) if lens is None else np.asarray(lens)
     dst = np.zeros(B, dtype=np.int64) if dst is None else np.asarray(dst)
     g = quant.PER_TENSOR if gran == "tensor" else quant.PER_HEAD
+    f = quant.E4M3 if fmt == "e4m3" else quant.E5M2
     cache = np.full((B, H, L, D), GUARD, dtype=np.uint8)
     if scale_in is None:
-        s = quant.quantize_kv(x, lens, dst, cache, g)
+        s = quant.quantize_kv(x, lens, dst, cache, g, f)
     else:
         s = np.asarray(scale_in, dtype=np.float32)
-        quant.fill_cache(x, lens, dst, cache, s, g)
+        quant.fill_cache(x, lens, dst, cache, s, g, f)
     return cache, s
 
 

@@ -5,6 +5,8 @@ Argument marshalling only: every step runs in the HIP kernels behind
 The functions keep the C names:
 
 * ``wa_kv_quant_fp8``  bf16 -> E4M3 KV-cache fill with dynamic or static scales
+  (``wa_kv_quant_fp8_fmt``: E4M3 or E5M2)
+* ``wa_kv_dequant_fp8``  float8 cache -> bf16
 * ``wa_encoder_attn``  dense bf16 attention (encoder, or causal prompt prefill)
 * ``wa_decode_attn``   one query token per sequence against an E4M3 cache
 
@@ -28,6 +30,9 @@ WA_ERR_HIP = 4
 WA_SCALE_PER_TENSOR = 0
 WA_SCALE_PER_HEAD = 1
 
+WA_FP8_E4M3 = 0
+WA_FP8_E5M2 = 1
+
 HEAD_DIM = 64
 
 
@@ -49,6 +54,10 @@ def _load():
     P, I, S, F, Z = ctypes.c_void_p, ctypes.c_int, Strides, ctypes.c_float, ctypes.c_size_t
     lib.wa_kv_quant_fp8.argtypes = [P, S, I, I, I, I, P, P, P, S, I, P, I, I, P, Z, P]
     lib.wa_kv_quant_fp8.restype = I
+    lib.wa_kv_quant_fp8_fmt.argtypes = [P, S, I, I, I, I, P, P, P, S, I, P, I, I, I, P, Z, P]
+    lib.wa_kv_quant_fp8_fmt.restype = I
+    lib.wa_kv_dequant_fp8.argtypes = [P, S, I, P, I, I, P, I, I, I, I, P, S, P]
+    lib.wa_kv_dequant_fp8.restype = I
     lib.wa_kv_quant_fp8_workspace_size.argtypes = [I, I, I, I]
     lib.wa_kv_quant_fp8_workspace_size.restype = Z
     lib.wa_encoder_attn.argtypes = [P, S, P, S, P, S, P, S, I, I, I, I, P, I, F, P]
@@ -66,7 +75,8 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn",
+EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_dequant_fp8",
+            "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn",
             "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
             "wa_status_string")
 
@@ -86,6 +96,14 @@ def _gran(g):
     if g in ("head", WA_SCALE_PER_HEAD):
         return WA_SCALE_PER_HEAD
     raise ValueError(f"scale granularity {g!r}")
+
+
+def _fmt(f):
+    if f in ("e4m3", WA_FP8_E4M3):
+        return WA_FP8_E4M3
+    if f in ("e5m2", WA_FP8_E5M2):
+        return WA_FP8_E5M2
+    raise ValueError(f"float8 format {f!r}")
 
 
 def _ptr(t):
@@ -140,6 +158,13 @@ def wa_kv_quant_fp8(x, cache, scale, gran, lens=None, dst_start=None, compute_sc
     ``scale`` (float32, [1] or [H]) is written when ``compute_scale`` and read
     otherwise.  ``lens``/``dst_start`` are int32 device tensors [B] or None.
     """
+    return wa_kv_quant_fp8_fmt(x, cache, scale, gran, "e4m3", lens, dst_start, compute_scale,
+                               workspace, stream)
+
+
+def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, compute_scale=True,
+                        workspace=None, stream=None):
+    """``wa_kv_quant_fp8`` with the format chosen: ``fmt`` is "e4m3" or "e5m2"."""
     _bits(x, torch.bfloat16)
     _bits(cache, torch.uint8)
     _bits(scale, torch.float32)
@@ -149,11 +174,32 @@ def wa_kv_quant_fp8(x, cache, scale, gran, lens=None, dst_start=None, compute_sc
         n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.wa_kv_quant_fp8(_ptr(x), _act_strides(x), B, H, T, D, _ptr(lens), _ptr(dst_start),
-                               _ptr(cache), _cache_strides(cache), cache.shape[2], _ptr(scale), g,
-                               int(bool(compute_scale)), _ptr(workspace), ws_bytes,
-                               _stream(x, stream)))
+    _check(lib.wa_kv_quant_fp8_fmt(_ptr(x), _act_strides(x), B, H, T, D, _ptr(lens),
+                                   _ptr(dst_start), _ptr(cache), _cache_strides(cache),
+                                   cache.shape[2], _ptr(scale), g, _fmt(fmt),
+                                   int(bool(compute_scale)), _ptr(workspace), ws_bytes,
+                                   _stream(x, stream)))
     return scale
+
+
+def wa_kv_dequant_fp8(cache, scale, gran, fmt, out=None, T_max=None, lens=None, stream=None):
+    """Read the uint8 ``cache`` [B][H][L][64] back as bf16 ``out`` [B][T][H][64]
+    (T = ``T_max``, default L): positions t < lens[b] (all when ``lens`` is
+    None) are written, the others are left as they are."""
+    _bits(cache, torch.uint8)
+    _bits(scale, torch.float32)
+    B, H, L, D = cache.shape
+    if out is None:
+        out = torch.empty((B, L if T_max is None else T_max, H, D), dtype=torch.bfloat16,
+                          device=cache.device)
+    _bits(out, torch.bfloat16)
+    if out.dim() != 4 or (out.shape[0], out.shape[2], out.shape[3]) != (B, H, D):
+        raise ValueError(f"out must be [B={B}][T][H={H}][{D}], got {tuple(out.shape)}")
+    T = out.shape[1]
+    _check(lib.wa_kv_dequant_fp8(_ptr(cache), _cache_strides(cache), L, _ptr(scale), _gran(gran),
+                                 _fmt(fmt), _ptr(lens), B, H, T, D, _ptr(out), _act_strides(out),
+                                 _stream(cache, stream)))
+    return out
 
 
 def wa_encoder_attn(q, k, v, out=None, lens=None, causal=False, softmax_scale=0.125, stream=None):

@@ -26,7 +26,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "e4m3_encode.h"
+#include "fp8_encode.h"
 #include "wa_internal.h"
 
 namespace wa {

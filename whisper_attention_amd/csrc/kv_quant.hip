@@ -1,9 +1,10 @@
-// bf16 -> OCP E4M3 KV-cache quantization for gfx950.
+// bf16 -> OCP float8 (E4M3, or E5M2) KV-cache quantization for gfx950.
 //
 // The dynamic per-tensor / per-head scaling of whisper-blaze 0.1.8 (PyPI
-// page, "Direct Kernel API": quantise_e4m3 returns codes and a scale) applied
-// to the KV cache that the HF blog "Blazingly fast whisper transcriptions
-// with Inference Endpoints" (section "Inference Stack") stores in one byte.
+// page, "Direct Kernel API": quantise_e4m3 returns codes and a scale; its
+// feature list names E4M3 and E5M2) applied to the KV cache that the HF blog
+// "Blazingly fast whisper transcriptions with Inference Endpoints" (section
+// "Inference Stack") stores in one byte.
 //
 // Work split.  A row (one token of one sequence) is H*64 bf16 = P pieces of
 // 16 bytes; piece p belongs to head p/8.  A block has lcm(64, P) threads when
@@ -21,14 +22,15 @@
 //                       (or the whole wave) and in LDS, one partial per block
 //                       and group, stored group-major.
 //   kv_scale_kernel     one block per group folds that group's partials and
-//                       writes scale[g] = amax_g / 448 (1 when amax_g is 0).
+//                       writes scale[g] = amax_g / FMAX (1 when amax_g is 0),
+//                       FMAX = 448 (E4M3) or 57344 (E5M2).
 //   kv_encode_kernel    divides each value by scale[g] (IEEE fp32 division),
-//                       clamps to +-448, converts pairs with the hardware OCP
-//                       fp8 conversion (round to nearest even) and writes 8
-//                       code bytes per piece into the cache slot.
+//                       clamps to +-FMAX, converts pairs with the hardware OCP
+//                       fp8/bf8 conversion (round to nearest even) and writes
+//                       8 code bytes per piece into the cache slot.
 #include <algorithm>
 
-#include "e4m3_encode.h"
+#include "fp8_encode.h"
 #include "wa_internal.h"
 
 namespace wa {
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(const uint16_t *__restric
 
 // One block per group: fold that group's n_blocks partials (contiguous).
 __global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restrict__ partial,
-                                                       int n_blocks, float *__restrict__ scale) {
+                                                       int n_blocks, float fmax,
+                                                       float *__restrict__ scale) {
   __shared__ uint32_t wmax[4];
   const int g = blockIdx.x;
   const uint32_t *pg = partial + (long)g * n_blocks;
@@ -135,10 +138,11 @@ __global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restric
   if (threadIdx.x == 0) {
     const uint32_t a = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     const float amax = __uint_as_float(a << 16);  // bf16 bits -> fp32, exact
-    scale[g] = amax == 0.0f ? 1.0f : amax / 448.0f;
+    scale[g] = amax == 0.0f ? 1.0f : amax / fmax;
   }
 }
 
+template <Fp8 F>
 __global__ __launch_bounds__(1024) void kv_encode_kernel(
     const uint16_t *__restrict__ x, wa_strides xs, int T_max, int P, int rows_per_pass,
     const int32_t *__restrict__ lens, const int32_t *__restrict__ dst_start,
@@ -170,13 +174,13 @@ __global__ __launch_bounds__(1024) void kv_encode_kernel(
 #pragma unroll
       for (int u = 0; u < kEncLoads; ++u) {
         const int t = t0 + ln.row + u * rpp;
-        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8_fast(v[u], s, r);
+        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8_fast<F>(v[u], s, r);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < kEncLoads; ++u) {
         const int t = t0 + ln.row + u * rpp;
-        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8(v[u], s);
+        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8<F>(v[u], s);
       }
     }
     if (rows_per_pass > 0) break;
@@ -218,7 +222,7 @@ size_t quant_workspace_bytes(const QuantPlan &p) {
 hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
                            const int32_t *lens, const int32_t *dst_start, uint8_t *cache,
                            wa_strides cs, int cache_len, float *scale, int per_head,
-                           int compute_scale, uint32_t *ws, const QuantPlan &plan,
+                           int compute_scale, Fp8 fmt, uint32_t *ws, const QuantPlan &plan,
                            hipStream_t stream) {
   (void)H;
   if (compute_scale) {
@@ -228,14 +232,16 @@ hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T
                        plan.groups, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const float fmax = fmt == Fp8::E4M3 ? fp8_max<Fp8::E4M3>() : fp8_max<Fp8::E5M2>();
     hipLaunchKernelGGL(kv_scale_kernel, dim3(plan.groups), dim3(256), 0, stream, ws,
-                       (int)plan.blocks, scale);
+                       (int)plan.blocks, fmax, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kv_encode_kernel, dim3(B, plan.enc_chunks), dim3(plan.threads), 0, stream, x,
-                     xs, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cache,
-                     cs, cache_len, scale, per_head);
+  auto kernel = fmt == Fp8::E4M3 ? kv_encode_kernel<Fp8::E4M3> : kv_encode_kernel<Fp8::E5M2>;
+  hipLaunchKernelGGL(kernel, dim3(B, plan.enc_chunks), dim3(plan.threads), 0, stream, x, xs, T_max,
+                     plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cache, cs, cache_len,
+                     scale, per_head);
   return hipGetLastError();
 }
 

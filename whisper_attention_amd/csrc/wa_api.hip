@@ -61,14 +61,15 @@ size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gra
   return wa::quant_workspace_bytes(wa::quant_plan(B, H, T_max, gran));
 }
 
-wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
-                          int head_dim, const int32_t *lens, const int32_t *dst_start,
-                          uint8_t *cache, wa_strides cs, int cache_len, float *scale,
-                          wa_scale_gran gran, int compute_scale, void *workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                              int head_dim, const int32_t *lens, const int32_t *dst_start,
+                              uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                              wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!x || !cache || !scale) return WA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || T_max <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
   if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (fmt != WA_FP8_E4M3 && fmt != WA_FP8_E5M2) return WA_ERR_INVALID_ARGUMENT;
   if (compute_scale != 0 && compute_scale != 1) return WA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64) return WA_ERR_UNSUPPORTED;
   if (H > 8192 || T_max > 65535 * 8) return WA_ERR_UNSUPPORTED;
@@ -83,7 +84,36 @@ wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_
   if (st != WA_OK) return st;
   return from_hip(wa::launch_kv_quant(x, xs, B, H, T_max, lens, dst_start, cache, cs, cache_len,
                                       scale, gran == WA_SCALE_PER_HEAD, compute_scale,
+                                      fmt == WA_FP8_E4M3 ? wa::Fp8::E4M3 : wa::Fp8::E5M2,
                                       static_cast<uint32_t *>(workspace), plan, stream));
+}
+
+wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                          int head_dim, const int32_t *lens, const int32_t *dst_start,
+                          uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                          wa_scale_gran gran, int compute_scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return wa_kv_quant_fp8_fmt(x, xs, B, H, T_max, head_dim, lens, dst_start, cache, cs, cache_len,
+                             scale, gran, WA_FP8_E4M3, compute_scale, workspace, workspace_bytes,
+                             stream);
+}
+
+wa_status wa_kv_dequant_fp8(const uint8_t *cache, wa_strides cs, int cache_len,
+                            const float *scale, wa_scale_gran gran, wa_fp8_format fmt,
+                            const int32_t *lens, int B, int H, int T_max, int head_dim,
+                            uint16_t *x, wa_strides xs, hipStream_t stream) {
+  if (!cache || !scale || !x) return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || T_max <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (fmt != WA_FP8_E4M3 && fmt != WA_FP8_E5M2) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535) return WA_ERR_UNSUPPORTED;
+  if (!bf16_layout_ok(x, xs) || !u8_layout_ok(cache, cs)) return WA_ERR_UNSUPPORTED;
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_kv_dequant(cache, cs, cache_len, scale, gran == WA_SCALE_PER_HEAD,
+                                        fmt == WA_FP8_E4M3 ? wa::Fp8::E4M3 : wa::Fp8::E5M2, lens,
+                                        B, H, T_max, x, xs, stream));
 }
 
 wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp8_encode.h"
 #include "wa.h"
 
 namespace wa {
@@ -26,8 +27,13 @@ size_t quant_workspace_bytes(const QuantPlan &p);
 hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
                            const int32_t *lens, const int32_t *dst_start, uint8_t *cache,
                            wa_strides cs, int cache_len, float *scale, int per_head,
-                           int compute_scale, uint32_t *ws, const QuantPlan &plan,
+                           int compute_scale, Fp8 fmt, uint32_t *ws, const QuantPlan &plan,
                            hipStream_t stream);
+
+// ---- dequantize -----------------------------------------------------------
+hipError_t launch_kv_dequant(const uint8_t *cache, wa_strides cs, int cache_len, const float *scale,
+                             int per_head, Fp8 fmt, const int32_t *lens, int B, int H, int T_max,
+                             uint16_t *x, wa_strides xs, hipStream_t stream);
 
 // ---- decode attention ---------------------------------------------------
 struct DecodePlan {
