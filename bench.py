@@ -44,7 +44,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # the kernel source they were taken on: a changed kernel reports null.
 TRAFFIC = {
     "encoder_attn.hip": ("04de279e6fbed296", {"encoder": 251.98e6, "prefill": 148.25e6}),
-    "decode_attn.hip": ("05856125f2689f36", {"cross": 246.21e6, "self": 42.13e6}),
+    "decode_attn.hip": ("bf7c58da424c2f68", {"cross": 246.21e6, "self": 42.13e6}),
+    "kv_dequant.hip": ("b81e378329bb8a7d", {"cross": 368.69e6}),
 }
 
 
@@ -332,7 +333,8 @@ def codec_rates(wl, steps):
     dq_bytes = 3.0 * B * H * L * HEAD_DIM          # 1 code byte read, 2 bf16 bytes written
     return {"kv_dequant": {"value": round(dq_bytes / (res["dequant"] * 1e-6) / 1e9, 1), "unit": "GB/s",
                            "frac": round(dq_bytes / (res["dequant"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                           "us": round(res["dequant"], 2),
+                           "us": round(res["dequant"], 2), "traffic": traffic("kv_dequant.hip", "cross"),
+                           "algorithmic_bytes": dq_bytes,
                            "note": f"E4M3 cache B={B} H={H} L={L} -> bf16, the {N_SETS} cache sets in turn"},
             "kv_quant_e5m2": {"value": round(wl.quant_bytes() / (res["quant_e5m2"] * 1e-6) / 1e9, 1),
                               "unit": "GB/s", "us": round(res["quant_e5m2"], 2),
