@@ -145,3 +145,25 @@ def test_deterministic(gpu):
     a = _gpu(wa, q, k, v, [700, 333], True)
     b = _gpu(wa, q, k, v, [700, 333], True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lam", [4.0, 10.0, 20.0, 100.0])
+def test_late_large_scores(gpu, lam, causal):
+    """Keys of later tiles scaled by lam: the scores of those tiles exceed
+    the earlier tiles' by about 4*lam bits (exp2 domain), so the running max
+    jumps in the middle of a row (and, for lam = 4, may stay within the lazy
+    rescale's 2^8 slack) -- in a full middle tile, in one key of an early
+    tile and in the ragged last tile."""
+    import whisper_attention_amd as wa
+    B, H, T = 2, 2, 700
+    announce(f"encoder late large scores lam={lam} causal={causal}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=11)
+    kf = k.float()
+    kf[0, 400:464] *= lam          # a whole middle tile
+    kf[0, 130:131] *= lam          # one key of an early tile
+    kf[1, 640:700] *= lam          # the ragged last tile
+    k = kf.to(torch.bfloat16)
+    lens = [700, 690]
+    got = _gpu(wa, q, k, v, lens, causal)
+    _check(got, q, k, v, lens, causal, f"late large scores lam={lam} causal={causal}")
