@@ -60,6 +60,22 @@ def dense_attention(q, k, v, lens, causal, softmax_scale, with_magnitude=False):
     return (out, mag) if with_magnitude else out
 
 
+def dense_attention_fp8qk(q_codes, q_scale, k_codes, k_scale, gran, v, lens, causal, softmax_scale,
+                          with_magnitude=False):
+    """Dense attention with Q and K given as E4M3 codes and dequantization scales.
+
+    The ``aggressive_fp8`` preset of whisper-blaze 0.1.8 (PyPI page,
+    "Precision Presets": FP8 everywhere) read for attention as Q and K stored
+    in float8 E4M3 with the quantize step's scales, V and the output in
+    bf16.  The attention is exactly ``dense_attention`` over the dequantized
+    values ``decode(code) * scale[g]`` (g = 0, or the head with per-head
+    scales).  q_codes, k_codes: uint8 [B][T][H][D]; v: [B][T][H][D].
+    """
+    qh = quant.dequantize(q_codes, q_scale, gran, head_axis=2)
+    kh = quant.dequantize(k_codes, k_scale, gran, head_axis=2)
+    return dense_attention(qh, kh, v, lens, causal, softmax_scale, with_magnitude)
+
+
 def decode_attention_dequant(q, khat, vhat, lens, softmax_scale, with_magnitude=False):
     """One query per (b, h) against already-dequantized keys and values.
 

@@ -199,3 +199,43 @@ def test_magnitude_is_weighted_abs_v():
     o2, m2 = attn.decode_attention_dequant(qd, kh, vh, [5, 2], 0.5, with_magnitude=True)
     o3 = attn.decode_attention_dequant(qd, kh, np.abs(vh), [5, 2], 0.5)
     np.testing.assert_allclose(m2, o3, rtol=1e-13)
+
+
+@pytest.mark.parametrize("gran", [quant.PER_TENSOR, quant.PER_HEAD])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8qk_is_attention_on_code_times_scale(gran, causal):
+    """Brute force with Python scalars on a tiny ragged batch: scores from
+    the decoded E4M3 codes times their scales (the per-head scale of head h
+    for both operands), the softmax, V in full precision."""
+    from oracle import e4m3
+    B, T, H, D = 2, 5, 2, 4
+    qc = workloads.fp8_codes((B, T, H, D), 3, 91).numpy()
+    kc = workloads.fp8_codes((B, T, H, D), 3, 92).numpy()
+    v = np.random.default_rng(5).standard_normal((B, T, H, D))
+    qs = np.float32([0.02, 0.5])[: (1 if gran == quant.PER_TENSOR else 2)]
+    ks = np.float32([0.25, 0.003])[: (1 if gran == quant.PER_TENSOR else 2)]
+    lens = [5, 3]
+    got = attn.dense_attention_fp8qk(qc, qs, kc, ks, gran, v, lens, causal, 0.125)
+    for b in range(B):
+        for h in range(H):
+            g = 0 if gran == quant.PER_TENSOR else h
+            for i in range(lens[b]):
+                keys = range(i + 1) if causal else range(lens[b])
+                s = [0.125 * sum(e4m3.decode(qc[b, i, h, d]) * float(qs[g]) *
+                                 e4m3.decode(kc[b, j, h, d]) * float(ks[g]) for d in range(D)) for j in keys]
+                w = [math.exp(x - max(s)) for x in s]
+                want = [sum(w[t] * v[b, j, h, d] for t, j in enumerate(keys)) / sum(w) for d in range(D)]
+                np.testing.assert_allclose(got[b, i, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8qk_scale_moves_between_q_and_k_and_softmax_scale():
+    """Only the product softmax_scale * q_scale * k_scale matters."""
+    B, T, H, D = 1, 7, 1, 64
+    qc = workloads.fp8_codes((B, T, H, D), 4, 93).numpy()
+    kc = workloads.fp8_codes((B, T, H, D), 4, 94).numpy()
+    v = np.random.default_rng(6).standard_normal((B, T, H, D))
+    a = attn.dense_attention_fp8qk(qc, np.float32([0.01]), kc, np.float32([0.04]), quant.PER_TENSOR, v,
+                                   [7], False, 0.125)
+    b = attn.dense_attention_fp8qk(qc, np.float32([0.04]), kc, np.float32([0.02]), quant.PER_TENSOR, v,
+                                   [7], False, 0.0625)
+    np.testing.assert_allclose(a, b, rtol=1e-12)
