@@ -368,6 +368,42 @@ def encoder_windows(steps, g_seed):
     return res
 
 
+def encoder_fp8qk(steps, g_seed):
+    """The encoder with E4M3 Q and K (wa_encoder_attn_fp8qk, per-tensor
+    scales) at the 30-s, 15-s and 10-s windows.  The codes are written once,
+    untimed, by the quantize kernel (the upstream projection's output in the
+    aggressive-fp8 reading); V stays bf16."""
+    import whisper_attention_amd as wa
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    res = {}
+    for name, B, T in (("30s", 16, 1500), ("15s", 64, 750), ("10s", 144, 500)):
+        H = 20
+        q, k, v = (gen_bf16((B, T, H, HEAD_DIM), g) for _ in range(3))
+        qc = torch.empty((B, T, H, HEAD_DIM), dtype=torch.uint8, device="cuda")
+        kc = torch.empty_like(qc)
+        qs = torch.empty(1, dtype=torch.float32, device="cuda")
+        ks = torch.empty_like(qs)
+        wa.wa_kv_quant_fp8(q, qc.permute(0, 2, 1, 3), qs, "tensor")
+        wa.wa_kv_quant_fp8(k, kc.permute(0, 2, 1, 3), ks, "tensor")
+        del q, k
+        o = torch.empty_like(v)
+        for _ in range(3):
+            wa.wa_encoder_attn_fp8qk(qc, qs, kc, ks, "tensor", v, out=o, softmax_scale=0.125)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            wa.wa_encoder_attn_fp8qk(qc, qs, kc, ks, "tensor", v, out=o, softmax_scale=0.125)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+        tf = 4.0 * B * H * T * T * HEAD_DIM / (us * 1e-6) / 1e12
+        res[name] = {"B": B, "T": T, "us": round(us, 2), "TFLOP/s": round(tf, 2)}
+        del qc, kc, v, o
+    res["note"] = "QK^T on the fp8 MFMA (E4M3 x E4M3), P.V in bf16; TFLOP/s counts 4*B*H*T^2*64"
+    return res
+
+
 def cpu_baseline(budget_s):
     """The CPU oracle on a bounded sample of the encoder workload: whole
     (b, h) pairs of B=16 x H=20 x T=1500 until ``budget_s`` seconds pass."""
@@ -435,6 +471,7 @@ def main():
     dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
     windows = encoder_windows(args.steps, g_seed=1)
+    enc_fp8 = encoder_fp8qk(args.steps, g_seed=3)
     graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
     codecs = codec_rates(wl, args.steps)
     if args.copy_calib:
@@ -497,6 +534,7 @@ def main():
                      "note": "two calls (K and V), each amax + scale + encode kernels"},
         **codecs,
         "encoder_windows": windows,
+        "encoder_fp8qk": enc_fp8,
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false> (encoder)",

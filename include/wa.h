@@ -8,6 +8,7 @@
  *   wa_kv_dequant_fp8  float8 cache -> bf16, the inverse read
  *   wa_encoder_attn  dense bf16 softmax attention (encoder self-attention,
  *                    or causal decoder prompt prefill), ragged by length
+ *                    (wa_encoder_attn_fp8qk: Q and K in E4M3)
  *   wa_decode_attn   one query token per sequence against an E4M3 KV cache
  *                    (decoder self-attention or cross-attention)
  *   wa_decode_attn_append  the same for decoder self-attention, with the
@@ -184,6 +185,34 @@ wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, w
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
                           int H, int T_max, int head_dim, const int32_t *lens, int causal,
                           float softmax_scale, hipStream_t stream);
+
+/*
+ * wa_encoder_attn_fp8qk -- wa_encoder_attn with Q and K given in float8 E4M3.
+ *
+ * What: whisper-blaze 0.1.8's "aggressive_fp8" preset (PyPI page, "Precision
+ *   Presets": FP8 everywhere) read for attention as Q and K stored as E4M3
+ *   codes with the quantize step's scales (V and the output stay bf16):
+ *     O = wa_encoder_attn(Q^, K^, V),  Q^ = decode(Qc) * q_scale[g],
+ *                                      K^ = decode(Kc) * k_scale[g]
+ *   with g = 0 (WA_SCALE_PER_TENSOR) or the head (WA_SCALE_PER_HEAD).  The
+ *   scores are taken on the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4,
+ *   fp32 result; its internal sums round at about 1e-4 of the sum of the
+ *   products' magnitudes), then scaled by softmax_scale * q_scale * k_scale.
+ *   Masks, lengths and rows not written are those of wa_encoder_attn.  The
+ *   codes are what wa_kv_quant_fp8 writes when given [B][T][H][64] strides.
+ *
+ * q, k       device uint8 [B][T_max][H][64] with strides qs, ks (in bytes:
+ *            16-byte aligned, strides multiples of 16).
+ * q_scale, k_scale  device float32 [1] or [H] (gran).
+ * v, o, lens, causal, softmax_scale, errors: as wa_encoder_attn; a null
+ *            scale is WA_ERR_INVALID_ARGUMENT.
+ */
+wa_status wa_encoder_attn_fp8qk(const uint8_t *q, wa_strides qs, const float *q_scale,
+                                const uint8_t *k, wa_strides ks, const float *k_scale,
+                                wa_scale_gran gran, const uint16_t *v, wa_strides vs, uint16_t *o,
+                                wa_strides os, int B, int H, int T_max, int head_dim,
+                                const int32_t *lens, int causal, float softmax_scale,
+                                hipStream_t stream);
 
 /*
  * wa_decode_attn -- one query token per sequence against an E4M3 KV cache.

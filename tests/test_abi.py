@@ -150,6 +150,28 @@ def test_encoder_validation(wa):
     assert _enc(wa, ks=_S(wa, h=65)) == wa.WA_ERR_UNSUPPORTED
 
 
+def _enc8(wa, **kw):
+    s = _S(wa)
+    a = dict(q=FAKE, qs=s, qsc=FAKE, k=FAKE, ks=s, ksc=FAKE, gran=0, v=FAKE, vs=s, o=FAKE, os=s, B=2, H=20,
+             T=1500, D=64, lens=None, causal=0, sc=0.125)
+    a.update(kw)
+    return wa.lib.wa_encoder_attn_fp8qk(a["q"], a["qs"], a["qsc"], a["k"], a["ks"], a["ksc"], a["gran"],
+                                        a["v"], a["vs"], a["o"], a["os"], a["B"], a["H"], a["T"], a["D"],
+                                        a["lens"], a["causal"], a["sc"], None)
+
+
+def test_encoder_fp8qk_validation(wa):
+    for name in ("q", "k", "v", "o", "qsc", "ksc"):
+        assert _enc8(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc8(wa, gran=5) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc8(wa, causal=3) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc8(wa, sc=-1.0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _enc8(wa, D=128) == wa.WA_ERR_UNSUPPORTED
+    assert _enc8(wa, q=MIS) == wa.WA_ERR_UNSUPPORTED
+    # uint8 Q/K strides must be multiples of 16 bytes
+    assert _enc8(wa, ks=_S(wa, t=20 * 64 + 8)) == wa.WA_ERR_UNSUPPORTED
+
+
 def _dec(wa, **kw):
     cs = wa.Strides(20 * 1500 * 64, 64, 1500 * 64)
     a = dict(q=FAKE, qs=wa.Strides(20 * 64, 0, 64), kc=FAKE, vc=FAKE, cs=cs, L=1500, ks=FAKE, vs=FAKE,

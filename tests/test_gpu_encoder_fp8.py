@@ -1,0 +1,139 @@
+"""GPU parity of wa_encoder_attn_fp8qk (E4M3 Q and K, bf16 V) against the
+oracle's attention over the dequantized codes (max-abs 2e-2, mean-abs 2e-3
+relative to max(1, M)).  Codes and scales come from the oracle's quantize of
+seeded bf16 Q and K (dynamic scales over the valid rows)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attn, quant
+from tests.gpu_helpers import announce, assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRAN = {"tensor": quant.PER_TENSOR, "head": quant.PER_HEAD}
+
+
+def _codes(x, lens, gran):
+    xf = x.float().numpy()
+    if lens is None:
+        lens = np.full(xf.shape[0], xf.shape[1])
+    s = quant.scales_from_amax(quant.group_amax(xf, lens, GRAN[gran]))
+    return quant.quantize(xf, s, GRAN[gran]), s
+
+
+def _run(wa, qc, qs, kc, ks, v, lens, causal, gran, views=None):
+    B, T, H, D = v.shape
+    if views is None:
+        qd, kd, vd = to_dev(qc), to_dev(kc), to_dev(v)
+    else:
+        qd, kd, vd = views
+    out = torch.full((B, T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wa.wa_encoder_attn_fp8qk(qd, to_dev(qs), kd, to_dev(ks), gran, vd, out=out,
+                             lens=None if lens is None else to_dev(np.asarray(lens, np.int32)),
+                             causal=causal, softmax_scale=0.125)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _check(got, qc, qs, kc, ks, v, lens, causal, gran, what, pairs=None):
+    B, T, H, _ = v.shape
+    lens_a = np.full(B, T) if lens is None else np.asarray(lens)
+    for b in range(B):
+        assert np.all(np.isnan(got[b, lens_a[b]:])), f"{what}: rows past len written"
+    g = GRAN[gran]
+    if pairs is None:
+        want, mag = attn.dense_attention_fp8qk(qc, qs, kc, ks, g, v.float().numpy(), lens_a, causal, 0.125,
+                                               with_magnitude=True)
+        mask = np.arange(T)[None, :] < lens_a[:, None]
+        assert_close(torch.from_numpy(got[mask]), want[mask], what, mag=mag[mask])
+        return
+    gs, ws, ms = [], [], []
+    for b, h in pairs:
+        n = lens_a[b]
+        sl = slice(h, h + 1)
+        sq = qs[h:h + 1] if g == quant.PER_HEAD else qs
+        sk = ks[h:h + 1] if g == quant.PER_HEAD else ks
+        w, m = attn.dense_attention_fp8qk(qc[b:b + 1, :, sl], sq, kc[b:b + 1, :, sl], sk, g,
+                                          v[b:b + 1, :, sl].float().numpy(), [n], causal, 0.125,
+                                          with_magnitude=True)
+        gs.append(got[b, :n, h])
+        ws.append(w[0, :n, 0])
+        ms.append(m[0, :n, 0])
+    assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what, mag=np.concatenate(ms))
+
+
+@pytest.mark.parametrize("gran", ["tensor", "head"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,T,lens", [(2, 3, 300, [300, 131]), (3, 2, 77, [77, 1, 64]), (1, 1, 1, [1]),
+                                        (2, 2, 129, [0, 129]), (2, 1, 257, [257, 250])])
+def test_ragged_shapes(gpu, B, H, T, lens, causal, gran):
+    import whisper_attention_amd as wa
+    announce(f"fp8qk ragged B={B} H={H} T={T} lens={lens} causal={causal} {gran}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=T + 1)
+    qc, qs = _codes(q, lens, gran)
+    kc, ks = _codes(k, lens, gran)
+    got = _run(wa, qc, qs, kc, ks, v, lens, causal, gran)
+    _check(got, qc, qs, kc, ks, v, lens, causal, gran, f"fp8qk B={B} T={T} causal={causal} {gran}")
+
+
+def test_large_v3_encoder_full_size_sampled(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["enc_l3"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    announce(f"fp8qk encoder large-v3 B={B} H={H} T={T} per-tensor (sampled (b, h))")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=0)
+    qc, qs = _codes(q, None, "tensor")
+    kc, ks = _codes(k, None, "tensor")
+    got = _run(wa, qc, qs, kc, ks, v, None, False, "tensor")
+    assert np.all(np.isfinite(got))
+    g = np.random.default_rng(2)
+    pairs = [(0, 0), (B - 1, H - 1)] + [(int(g.integers(B)), int(g.integers(H))) for _ in range(6)]
+    _check(got, qc, qs, kc, ks, v, None, False, "tensor", "fp8qk enc-L3", pairs=pairs)
+
+
+def test_prefill_causal_full_size_per_head(gpu):
+    """The prefill shape (B=128 H=20 T=224, lengths U[4,224]) with x20
+    outliers in K, per-head scales, causal."""
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["prefill"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    announce(f"fp8qk prefill B={B} H={H} T={T} causal per-head")
+    lens = workloads.lens_uniform(B, cfg["lo"], cfg["hi"], 0)
+    q, k, v = workloads.prefill_inputs(B, H, T, cfg["lo"], cfg["hi"], cfg["outlier_p"], cfg["outlier_mult"],
+                                       seed=0)[:3]
+    qc, qs = _codes(q, lens, "head")
+    kc, ks = _codes(k, lens, "head")
+    got = _run(wa, qc, qs, kc, ks, v, lens, True, "head")
+    _check(got, qc, qs, kc, ks, v, lens, True, "head", "fp8qk prefill")
+
+
+def test_codes_from_the_quantize_kernel_and_strided_views(gpu):
+    """Q and K codes written by wa_kv_quant_fp8 into [B][T][H][64] storage
+    (cache strides over that layout), then read by the attention through
+    views of wider storage.  The kernel's codes and scales must equal the
+    oracle's bit for bit; the expected output uses the oracle's."""
+    import whisper_attention_amd as wa
+    B, H, T = 3, 4, 200
+    announce(f"fp8qk codes from the quantize kernel B={B} H={H} T={T}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=21)
+    lens = [200, 150, 33]
+    ld = to_dev(np.asarray(lens, np.int32))
+    big = torch.zeros((2, B, T, H + 2, 64), dtype=torch.uint8, device="cuda")
+    qv, kv = big[0, :, :, 1:H + 1], big[1, :, :, 1:H + 1]          # [B][T][H][64] views
+    qsd = torch.zeros(H, dtype=torch.float32, device="cuda")
+    ksd = torch.zeros(H, dtype=torch.float32, device="cuda")
+    wa.wa_kv_quant_fp8(to_dev(q), qv.permute(0, 2, 1, 3), qsd, "head", lens=ld)
+    wa.wa_kv_quant_fp8(to_dev(k), kv.permute(0, 2, 1, 3), ksd, "head", lens=ld)
+    vd = to_dev(v)
+    out = torch.full((B, T, H, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wa.wa_encoder_attn_fp8qk(qv, qsd, kv, ksd, "head", vd, out=out, lens=ld, causal=False, softmax_scale=0.125)
+    torch.cuda.synchronize()
+    qc, qs = _codes(q, lens, "head")
+    kc, ks = _codes(k, lens, "head")
+    valid = np.arange(T)[None, :] < np.asarray(lens)[:, None]
+    for got_c, want_c, got_s, want_s in ((qv, qc, qsd, qs), (kv, kc, ksd, ks)):
+        assert np.array_equal(got_s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+        assert np.array_equal(got_c.cpu().numpy()[valid], want_c[valid])
+    _check(out.float().cpu().numpy(), qc, qs, kc, ks, v, lens, False, "head", "fp8qk from quantize kernel")

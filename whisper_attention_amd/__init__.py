@@ -8,9 +8,10 @@ The functions keep the C names:
   (``wa_kv_quant_fp8_fmt``: E4M3 or E5M2)
 * ``wa_kv_dequant_fp8``  float8 cache -> bf16
 * ``wa_encoder_attn``  dense bf16 attention (encoder, or causal prompt prefill)
+  (``wa_encoder_attn_fp8qk``: E4M3 Q and K)
 * ``wa_decode_attn``   one query token per sequence against an E4M3 cache
 
-The library must have been built (``python -m whisper_attention_amd.build``);
+The library must have been built (``python whisper_attention_amd/build.py``);
 importing fails loudly when it is missing -- there is no fallback.
 """
 import ctypes
@@ -49,7 +50,7 @@ class WaError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m whisper_attention_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python whisper_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S, F, Z = ctypes.c_void_p, ctypes.c_int, Strides, ctypes.c_float, ctypes.c_size_t
     lib.wa_kv_quant_fp8.argtypes = [P, S, I, I, I, I, P, P, P, S, I, P, I, I, P, Z, P]
@@ -62,6 +63,8 @@ def _load():
     lib.wa_kv_quant_fp8_workspace_size.restype = Z
     lib.wa_encoder_attn.argtypes = [P, S, P, S, P, S, P, S, I, I, I, I, P, I, F, P]
     lib.wa_encoder_attn.restype = I
+    lib.wa_encoder_attn_fp8qk.argtypes = [P, S, P, P, S, P, I, P, S, P, S, I, I, I, I, P, I, F, P]
+    lib.wa_encoder_attn_fp8qk.restype = I
     lib.wa_decode_attn.argtypes = [P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
     lib.wa_decode_attn.restype = I
     lib.wa_decode_attn_append.argtypes = [P, S, P, P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
@@ -76,7 +79,7 @@ def _load():
 lib = _load()
 
 EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_dequant_fp8",
-            "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn",
+            "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn", "wa_encoder_attn_fp8qk",
             "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
             "wa_status_string")
 
@@ -213,6 +216,27 @@ def wa_encoder_attn(q, k, v, out=None, lens=None, causal=False, softmax_scale=0.
                                _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
                                _ptr(lens), int(bool(causal)), float(softmax_scale),
                                _stream(q, stream)))
+    return out
+
+
+def wa_encoder_attn_fp8qk(q, q_scale, k, k_scale, gran, v, out=None, lens=None, causal=False,
+                          softmax_scale=0.125, stream=None):
+    """Dense attention with E4M3 Q and K (uint8 [B][T][H][64] codes, float32
+    scales [1] or [H]) and bf16 V [B][T][H][64]; returns ``out`` (bf16)."""
+    _bits(q, torch.uint8)
+    _bits(k, torch.uint8)
+    _bits(v, torch.bfloat16)
+    _bits(q_scale, torch.float32)
+    _bits(k_scale, torch.float32)
+    B, T, H, D = v.shape
+    if q.shape != v.shape or k.shape != v.shape:
+        raise ValueError("q, k and v must share the [B][T][H][64] shape")
+    if out is None:
+        out = torch.empty_like(v)
+    _check(lib.wa_encoder_attn_fp8qk(_ptr(q), _act_strides(q), _ptr(q_scale), _ptr(k), _act_strides(k),
+                                     _ptr(k_scale), _gran(gran), _ptr(v), _act_strides(v), _ptr(out),
+                                     _act_strides(out), B, H, T, D, _ptr(lens), int(bool(causal)),
+                                     float(softmax_scale), _stream(v, stream)))
     return out
 
 

@@ -1,6 +1,7 @@
 """Build libwa.so (the C-ABI HIP library) in-tree for gfx950.
 
-Run as ``python -m whisper_attention_amd.build``; ``__graft_entry__.build()``
+Run as ``python whisper_attention_amd/build.py`` (by path: importing the package
+would load the library before it is rebuilt); ``__graft_entry__.build()``
 calls :func:`build`.  Every call compiles from source.
 """
 import glob

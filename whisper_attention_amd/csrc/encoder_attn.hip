@@ -54,6 +54,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -65,7 +66,7 @@ constexpr int kBM = kWaves * kQW;         // queries per block
 constexpr int kCopies = 2;                // 8-row copy instructions per wave per K/V tile
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
-constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+constexpr int kStageBytes = 2 * kTileBytes;  // K then V (an fp8 K tile uses the first half of its slot)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;             // lazy-rescale threshold, log2 units
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -117,6 +118,21 @@ __device__ __forceinline__ CopyOffsets copy_offsets(wa_strides ks, wa_strides vs
   return CopyOffsets{(uint32_t)((r * ks.t + chunk * 8) * 2), (uint32_t)((r * vs.t + chunk * 8) * 2)};
 }
 
+// fp8 K tiles: 64-byte rows, four 16-byte chunks, chunk index XORed with
+// bits 2 and 3 of the row.  The 16 lanes of a K operand read (rows 0..15 in
+// the permuted order, one chunk) then cover all 16 slots of 256 bytes.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 2) & 1) | (((row >> 3) & 1) << 1); }
+__device__ __forceinline__ int lds_off8(int row, int chunk) { return row * 64 + ((chunk ^ swz8(row)) << 4); }
+
+// Per-lane byte offset of the fp8 K row this lane copies: one copy
+// instruction fills rows [row0, row0+16), lane l landing in 16-byte LDS slot
+// l; rows at or past kend are clamped to row kend-1.
+__device__ __forceinline__ uint32_t copy_offset_k8(wa_strides ks, int max_row, int lane, int row0) {
+  const int row = row0 + (lane >> 2);
+  const int chunk = (lane & 3) ^ swz8(row);
+  return (uint32_t)(min(row, max_row) * ks.t + chunk * 16);
+}
+
 // The LDS ring: four stages of one K tile and one V tile each.
 __shared__ __attribute__((aligned(1024))) uint8_t g_lds[4][kStageBytes];
 
@@ -144,17 +160,26 @@ __device__ __forceinline__ uint32_t lds_addr(int stage) {
 // Issue the asynchronous copy of the K/V tile that starts at row k0 into a
 // stage.  Wave w fills K rows and V rows [16w, 16w+16) of the stage, 8 rows
 // per copy instruction.
-__device__ __forceinline__ void issue_tile(int stage, const uint16_t *kp, wa_strides ks,
+// With fp8 K (kFp8) the K tile is 4 KB: one 16-row copy per wave, rows
+// [16w, 16w+16), from byte offsets k8 (the full-tile offset) of a uint8 K.
+template <bool kFp8>
+__device__ __forceinline__ void issue_tile(int stage, const void *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
-                                           const CopyOffsets (&full)[kCopies], int lane, int w) {
+                                           const CopyOffsets (&full)[kCopies], uint32_t k8, int lane,
+                                           int w) {
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) {
     const int row0 = (w * kCopies + i) * 8;
     // only the last tile can run past kend
     const CopyOffsets c = k0 + kBN <= kend ? full[i] : copy_offsets(ks, vs, kend - 1 - k0, lane, row0);
     const uint32_t dst = lds_addr(stage) + row0 * 128;
-    copy16_to_lds(kp + (long)k0 * ks.t, c.k, dst);
+    if (!kFp8) copy16_to_lds(static_cast<const uint16_t *>(kp) + (long)k0 * ks.t, c.k, dst);
     copy16_to_lds(vp + (long)k0 * vs.t, c.v, dst + kTileBytes);
+  }
+  if (kFp8) {
+    const int row0 = w * 16;
+    const uint32_t off = k0 + kBN <= kend ? k8 : copy_offset_k8(ks, kend - 1 - k0, lane, row0);
+    copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, lds_addr(stage) + row0 * 64);
   }
 }
 
@@ -170,6 +195,7 @@ struct WaveState {
 // Per-lane LDS byte offsets of the operand reads (the same in every tile).
 struct ReadOffsets {
   int k[4];    // K rows for MFMA c (key block 0; key block 1 is +4096)
+  int k8[2];   // fp8 K: the lane's two 16-byte chunks (key block 1 is +2048)
   int v[2][2]; // V^T transposing reads for (db, th); key chunk c is +2048*c
 };
 
@@ -179,6 +205,9 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
   const int krow = swap_bits23(col);
 #pragma unroll
   for (int c = 0; c < 4; ++c) r.k[c] = lds_off(krow, c * 2 + half);
+  // fp8: operand byte b of lane group `half` is dim 32*half + b
+  r.k8[0] = lds_off8(krow, 2 * half);
+  r.k8[1] = lds_off8(krow, 2 * half + 1);
   // transposing read: source lane a = lane & 15 points at key row
   // c*16 + th*4 + half*8 + a/4 and dims db*32 + ((lane>>4)&1)*16 + (a%4)*4
   const int a = lane & 15;
@@ -196,8 +225,28 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
 // S^T = K . Q^T for one key tile: each K fragment feeds both query blocks.
 // s[kb][qb][r] is the score of query (qb*32 + col) and key
 // kb*32 + (r/8)*16 + half*8 + r%8 of the tile.
+template <bool kFp8>
 __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
                                        const ReadOffsets &ro, f32x16 (&s)[2][2]) {
+  if (kFp8) {
+    // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3): the whole head dim in one
+    // instruction; lane l gives K row l%32 and Q column l%32, dims
+    // 32*(l/32) .. +32 in byte order
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 a0 = *reinterpret_cast<const uint4 *>(kl + ro.k8[0] + kb * 2048);
+      const uint4 a1 = *reinterpret_cast<const uint4 *>(kl + ro.k8[1] + kb * 2048);
+      const i32x8 ka = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const uint4 b0 = __builtin_bit_cast(uint4, st.qreg[qb][0]);
+        const uint4 b1 = __builtin_bit_cast(uint4, st.qreg[qb][1]);
+        const i32x8 qv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        s[kb][qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qv, f32x16{}, 0, 0, 0, 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     bf16x8 ka[4];
@@ -341,9 +390,11 @@ __device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
 }
 
 struct Ctx {
-  const uint16_t *kp, *vp;
+  const void *kp;
+  const uint16_t *vp;
   wa_strides ks, vs;
   CopyOffsets co[kCopies];
+  uint32_t k8;     // fp8 K: this lane's copy offset within a full tile
   ReadOffsets ro;
   int nt, kend, len, wq_lo, lane, w;
   float c_log2;
@@ -352,23 +403,26 @@ struct Ctx {
 // Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+2 is
 // copied into `ahead` (the stage of tile t-2, whose last reads were in
 // interval t-1).  The block's waves pass one barrier per interval.
+template <bool kFp8>
 __device__ __forceinline__ void open_interval(int ahead, int t, const Ctx &x) {
   // Keep every instruction of the previous interval above the barrier.
   __builtin_amdgcn_sched_barrier(0);
-  // This wave's copies of tile t are complete -- only tile t+1's 2*kCopies
-  // copies may still be in flight -- and so are its LDS reads of interval
+  // This wave's copies of tile t are complete -- only tile t+1's copies
+  // (2*kCopies, or kCopies + 1 with fp8 K) may still be in flight -- and so
+  // are its LDS reads of interval
   // t-1 (the immediate holds vmcnt in bits 3:0 and lgkmcnt 0).  Then a bare
   // barrier (a workgroup fence would wait for tile t+1's copies too):
   // afterwards tile t is in LDS for everyone and the stage of tile t-2 is free.
   if (t + 1 < x.nt)
-    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0 + 2 * kCopies);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0 + (kFp8 ? kCopies + 1 : 2 * kCopies));
   else
     __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if (t + 2 < x.nt) issue_tile(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.lane, x.w);
+  if (t + 2 < x.nt)
+    issue_tile<kFp8>(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
@@ -380,14 +434,14 @@ __device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
 // Interval t: P(t-1).V(t-1) and S(t) on the matrix cores, then the softmax
 // of tile t on the vector ALU (the other block on the CU fills the matrix
 // cores meanwhile).  P(t) is carried to the next interval in `pa`.
-template <bool kCausal>
+template <bool kCausal, bool kFp8>
 __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
                                          const uint8_t *prev, int ahead, int t, const Ctx &x) {
-  open_interval(ahead, t, x);
+  open_interval<kFp8>(ahead, t, x);
   if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
   if (wave_needs<kCausal>(t, x)) {
     f32x16 s[2][2];
-    scores(st, cur, x.ro, s);
+    scores<kFp8>(st, cur, x.ro, s);
     __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
     float alpha[2];
     if (tile_max<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, alpha))
@@ -404,11 +458,14 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], cons
   }
 }
 
-template <bool kCausal>
+// kFp8: q and k hold E4M3 codes (uint8, strides in bytes) with
+// dequantization scales q_scale / k_scale ([1], or [H] when per_head).
+template <bool kCausal, bool kFp8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
-    const uint16_t *__restrict__ q, wa_strides qs, const uint16_t *__restrict__ k, wa_strides ks,
+    const void *__restrict__ q, wa_strides qs, const void *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
-    int T_max, const int32_t *__restrict__ lens, float c_log2, int n_qt, int total) {
+    int T_max, const int32_t *__restrict__ lens, float c_log2, const float *__restrict__ q_scale,
+    const float *__restrict__ k_scale, int per_head, int n_qt, int total) {
   // XCD-aware order: blocks are dispatched round robin over the 8 XCDs, so
   // block L runs on XCD L % 8.  Give each XCD a contiguous run of work items
   // so the query tiles of one (b, h) share that XCD's L2 copy of K and V.
@@ -426,7 +483,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   Ctx x;
-  x.kp = k + (long)b * ks.b + (long)h * ks.h;
+  x.kp = kFp8 ? (const void *)(static_cast<const uint8_t *>(k) + (long)b * ks.b + (long)h * ks.h)
+              : (const void *)(static_cast<const uint16_t *>(k) + (long)b * ks.b + (long)h * ks.h);
   x.vp = v + (long)b * vs.b + (long)h * vs.h;
   x.ks = ks;
   x.vs = vs;
@@ -436,21 +494,35 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   x.wq_lo = q0 + w * kQW;
   x.lane = lane;
   x.w = w;
-  x.c_log2 = c_log2;
+  // fp8: the scores come out in code units; fold both scales into the
+  // exp2-domain multiplier
+  x.c_log2 = kFp8 ? c_log2 * q_scale[per_head ? h : 0] * k_scale[per_head ? h : 0] : c_log2;
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopies + i) * 8);
-  issue_tile(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, lane, w);
-  if (x.nt > 1) issue_tile(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, lane, w);
+  x.k8 = copy_offset_k8(ks, kBN - 1, lane, w * 16);
+  issue_tile<kFp8>(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
+  if (x.nt > 1) issue_tile<kFp8>(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, x.k8, lane, w);
   x.ro = read_offsets(lane);
 
   WaveState st;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int my_q = x.wq_lo + qb * 32 + col;
-    const uint16_t *qp = q + (long)b * qs.b + (long)my_q * qs.t + (long)h * qs.h + half * 8;
+    if (kFp8) {
+      // 32 code bytes, dims 32*half .. +32, in qreg[qb][0..1]
+      const uint8_t *qp = static_cast<const uint8_t *>(q) + (long)b * qs.b + (long)my_q * qs.t +
+                          (long)h * qs.h + half * 32;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st.qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+      for (int c = 0; c < 2; ++c)
+        st.qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+      st.qreg[qb][2] = st.qreg[qb][3] = bf16x8{};
+    } else {
+      const uint16_t *qp = static_cast<const uint16_t *>(q) + (long)b * qs.b + (long)my_q * qs.t +
+                           (long)h * qs.h + half * 8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st.qreg[qb][c] = my_q < len ? *reinterpret_cast<const bf16x8 *>(qp + c * 16) : bf16x8{};
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db) st.oacc[db][qb] = f32x16{};
     st.lacc[qb] = f32x4{};
@@ -467,13 +539,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   // is j % 4.
   bf16x8 pa[2][4];
   for (int t = 0; t <= x.nt; t += 4) {
-    interval<kCausal>(st, pa, g_lds[0], g_lds[3], 2, t, x);
+    interval<kCausal, kFp8>(st, pa, g_lds[0], g_lds[3], 2, t, x);
     if (t + 1 > x.nt) break;
-    interval<kCausal>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
+    interval<kCausal, kFp8>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
     if (t + 2 > x.nt) break;
-    interval<kCausal>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
+    interval<kCausal, kFp8>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
     if (t + 3 > x.nt) break;
-    interval<kCausal>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
+    interval<kCausal, kFp8>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
   }
 
 #pragma unroll
@@ -503,20 +575,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 
 }  // namespace
 
-hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_strides ks,
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
-                          int H, int T_max, const int32_t *lens, int causal,
-                          float softmax_scale, hipStream_t stream) {
+                          int H, int T_max, const int32_t *lens, int causal, float softmax_scale,
+                          const float *q_scale, const float *k_scale, int per_head, hipStream_t stream) {
   const float c_log2 = softmax_scale * kLog2e;
   const int n_qt = (T_max + kBM - 1) / kBM;
   const long total = (long)B * H * n_qt;
   const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(kWaves * 64);
-  if (causal)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H,
-                       T_max, lens, c_log2, n_qt, (int)total);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H,
-                       T_max, lens, c_log2, n_qt, (int)total);
+  const bool fp8 = q_scale != nullptr;
+  auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
+                       : (fp8 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H, T_max, lens,
+                     c_log2, q_scale, k_scale, per_head, n_qt, (int)total);
   return hipGetLastError();
 }
 

@@ -132,7 +132,29 @@ wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, w
   wa_status st = check_device();
   if (st != WA_OK) return st;
   return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
-                                     softmax_scale, stream));
+                                     softmax_scale, nullptr, nullptr, 0, stream));
+}
+
+wa_status wa_encoder_attn_fp8qk(const uint8_t *q, wa_strides qs, const float *q_scale,
+                                const uint8_t *k, wa_strides ks, const float *k_scale,
+                                wa_scale_gran gran, const uint16_t *v, wa_strides vs, uint16_t *o,
+                                wa_strides os, int B, int H, int T_max, int head_dim,
+                                const int32_t *lens, int causal, float softmax_scale,
+                                hipStream_t stream) {
+  if (!q || !k || !v || !o || !q_scale || !k_scale) return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || T_max <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return WA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  if (!u8_layout_ok(q, qs) || !u8_layout_ok(k, ks) || !bf16_layout_ok(v, vs) || !bf16_layout_ok(o, os))
+    return WA_ERR_UNSUPPORTED;
+  if ((long)B * H * ((T_max + 127) / 128) > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
+                                     softmax_scale, q_scale, k_scale, gran == WA_SCALE_PER_HEAD,
+                                     stream));
 }
 
 size_t wa_decode_attn_workspace_size(int B, int H, int cache_len) {

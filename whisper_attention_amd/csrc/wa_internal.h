@@ -53,9 +53,12 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
                          wa_strides ns = wa_strides{0, 0, 0});
 
 // ---- encoder / prefill attention ----------------------------------------
-hipError_t launch_encoder(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+// q_scale == nullptr: bf16 Q and K.  Otherwise Q and K are E4M3 codes with
+// those dequantization scales ([1], or [H] when per_head).
+hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_strides ks,
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
-                          int H, int T_max, const int32_t *lens, int causal,
-                          float softmax_scale, hipStream_t stream);
+                          int H, int T_max, const int32_t *lens, int causal, float softmax_scale,
+                          const float *q_scale, const float *k_scale, int per_head,
+                          hipStream_t stream);
 
 }  // namespace wa
