@@ -44,6 +44,11 @@
 // FMA per score), with a lazy rescale -- the running max moves only when a
 // tile max exceeds it by more than 2^8 -- and row sums of the bf16 weights
 // taken on the matrix pipe by a small 16x16x32 MFMA per key chunk.
+//
+// fp8 Q and K (kFp8, the aggressive-fp8 variant): E4M3 codes with
+// dequantization scales.  K tiles are 4 KB (64-byte rows) and S^T comes from
+// one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block; the scales join the
+// exp2-domain multiplier, and everything after the scores is unchanged.
 #include <cmath>
 
 #include "wa_internal.h"
