@@ -43,7 +43,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # counts are in profiles/hbm_traffic_counters.md), with the sha256 prefix of
 # the kernel source they were taken on: a changed kernel reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("04de279e6fbed296", {"encoder": 251.98e6, "prefill": 148.25e6}),
+    "encoder_attn.hip": ("91473fdc834d89e4", {"encoder": 251.98e6, "prefill": 148.25e6,
+                                              "fp8qk_30s": 190.51e6}),
     "decode_attn.hip": ("bf7c58da424c2f68", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("b81e378329bb8a7d", {"cross": 368.69e6}),
 }
@@ -399,6 +400,10 @@ def encoder_fp8qk(steps, g_seed):
         us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
         tf = 4.0 * B * H * T * T * HEAD_DIM / (us * 1e-6) / 1e12
         res[name] = {"B": B, "T": T, "us": round(us, 2), "TFLOP/s": round(tf, 2)}
+        if name == "30s":
+            # 1 B of Q and of K codes, 2 B of V and of O per element
+            res[name]["algorithmic_bytes"] = 6.0 * B * T * H * HEAD_DIM
+            res[name]["traffic"] = traffic("encoder_attn.hip", "fp8qk_30s")
         del qc, kc, v, o
     res["note"] = "QK^T on the fp8 MFMA (E4M3 x E4M3), P.V in bf16; TFLOP/s counts 4*B*H*T^2*64"
     return res
