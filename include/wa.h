@@ -38,6 +38,9 @@
  *     and their b/t/h strides multiples of 8; uint8 cache pointers and
  *     workspaces 16-byte aligned, cache strides multiples of 16
  *     (WA_ERR_UNSUPPORTED otherwise).
+ *   - The encoder calls address a row of K or V within 64 rows with a 31-bit
+ *     byte offset: a position stride (ks.t, vs.t) of 2^24 elements or more
+ *     (2^25 for E4M3 codes) is WA_ERR_UNSUPPORTED.
  *   - Argument checks run on the host before any HIP call and launch nothing
  *     on failure.  The first call on a device checks that it is a gfx950
  *     (WA_ERR_UNSUPPORTED otherwise).  A failed launch returns WA_ERR_HIP.

@@ -148,6 +148,9 @@ def test_encoder_validation(wa):
     assert _enc(wa, D=80) == wa.WA_ERR_UNSUPPORTED
     assert _enc(wa, o=MIS) == wa.WA_ERR_UNSUPPORTED
     assert _enc(wa, ks=_S(wa, h=65)) == wa.WA_ERR_UNSUPPORTED
+    # a position stride whose 64-row tile does not fit a 32-bit byte offset
+    assert _enc(wa, vs=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
+    assert _enc(wa, ks=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
 
 
 def _enc8(wa, **kw):
@@ -170,6 +173,8 @@ def test_encoder_fp8qk_validation(wa):
     assert _enc8(wa, q=MIS) == wa.WA_ERR_UNSUPPORTED
     # uint8 Q/K strides must be multiples of 16 bytes
     assert _enc8(wa, ks=_S(wa, t=20 * 64 + 8)) == wa.WA_ERR_UNSUPPORTED
+    assert _enc8(wa, ks=_S(wa, t=1 << 25)) == wa.WA_ERR_UNSUPPORTED
+    assert _enc8(wa, vs=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
 
 
 def _dec(wa, **kw):

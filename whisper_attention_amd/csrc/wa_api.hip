@@ -41,6 +41,12 @@ wa_status check_device() {
 
 wa_status from_hip(hipError_t e) { return e == hipSuccess ? WA_OK : WA_ERR_HIP; }
 
+// A row within 64 rows at a position stride of t elements of elem_bytes (2 or
+// 1), addressed with a 31-bit byte offset: t below 2^24 (bf16) or 2^25 (E4M3).
+bool tile_rows_fit(int64_t t, int elem_bytes) {
+  return t >= 0 && t < (int64_t(1) << (elem_bytes == 2 ? 24 : 25));
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +135,9 @@ wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, w
       !bf16_layout_ok(o, os))
     return WA_ERR_UNSUPPORTED;
   if ((long)B * H * ((T_max + 127) / 128) > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  // the tile copies address a K or V row within a 64-row tile with a 32-bit
+  // byte offset
+  if (!tile_rows_fit(ks.t, 2) || !tile_rows_fit(vs.t, 2)) return WA_ERR_UNSUPPORTED;
   wa_status st = check_device();
   if (st != WA_OK) return st;
   return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
@@ -150,6 +159,7 @@ wa_status wa_encoder_attn_fp8qk(const uint8_t *q, wa_strides qs, const float *q_
   if (!u8_layout_ok(q, qs) || !u8_layout_ok(k, ks) || !bf16_layout_ok(v, vs) || !bf16_layout_ok(o, os))
     return WA_ERR_UNSUPPORTED;
   if ((long)B * H * ((T_max + 127) / 128) > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  if (!tile_rows_fit(ks.t, 1) || !tile_rows_fit(vs.t, 2)) return WA_ERR_UNSUPPORTED;
   wa_status st = check_device();
   if (st != WA_OK) return st;
   return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
