@@ -4,7 +4,8 @@
  * Operations, all asynchronous on the caller's HIP stream:
  *
  *   wa_kv_quant_fp8  bf16 -> float8 E4M3 quantization that fills a KV cache
- *                    (wa_kv_quant_fp8_fmt: E4M3 or E5M2)
+ *                    (wa_kv_quant_fp8_fmt: E4M3 or E5M2; wa_kv_quant_fp8_kv:
+ *                    K and V in one call)
  *   wa_kv_dequant_fp8  float8 cache -> bf16, the inverse read
  *   wa_encoder_attn  dense bf16 softmax attention (encoder self-attention,
  *                    or causal decoder prompt prefill), ragged by length
@@ -138,6 +139,29 @@ wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, in
                               uint8_t *cache, wa_strides cs, int cache_len, float *scale,
                               wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * wa_kv_quant_fp8_kv -- wa_kv_quant_fp8_fmt for a layer's keys and values in
+ * one call.
+ *
+ * What: exactly two wa_kv_quant_fp8_fmt calls, (k -> k_cache, k_scale) and
+ *   (v -> v_cache, v_scale), with their own scale groups (the cache fill of
+ *   the HF blog's "Inference Stack" stores both K and V in one byte), run as
+ *   one launch per kernel instead of two.  K and V share B, H, T_max, lens,
+ *   dst_start, the cache layout cs and cache_len; their activation strides
+ *   ks and vs may differ.
+ *
+ * workspace  device scratch of at least 2 * wa_kv_quant_fp8_workspace_size()
+ *            bytes when compute_scale = 1.
+ * Errors: those of wa_kv_quant_fp8_fmt; a null v, v_cache or v_scale is
+ *   WA_ERR_INVALID_ARGUMENT.
+ */
+wa_status wa_kv_quant_fp8_kv(const uint16_t *k, wa_strides ks, const uint16_t *v, wa_strides vs,
+                             int B, int H, int T_max, int head_dim, const int32_t *lens,
+                             const int32_t *dst_start, uint8_t *k_cache, uint8_t *v_cache,
+                             wa_strides cs, int cache_len, float *k_scale, float *v_scale,
+                             wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * wa_kv_dequant_fp8 -- read a float8 KV cache back as bf16.

@@ -106,6 +106,26 @@ def test_quant_fmt_validation(wa):
         assert _quant_fmt(wa, fmt, wsb=16) == wa.WA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_quant_pair_validation(wa):
+    S = _S(wa)
+    cs = wa.Strides(20 * 1500 * 64, 64, 1500 * 64)
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, ksc=FAKE, vsc=FAKE, gran=0, fmt=0, wsb=0, D=64, vs=S)
+        a.update(kw)
+        return wa.lib.wa_kv_quant_fp8_kv(a["k"], S, a["v"], a["vs"], 2, 20, 1500, a["D"], None, None, a["kc"],
+                                         a["vc"], cs, 1500, a["ksc"], a["vsc"], a["gran"], a["fmt"], 1, FAKE,
+                                         a["wsb"], None)
+    for name in ("k", "v", "kc", "vc", "ksc", "vsc"):
+        assert call(**{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert call(fmt=2) == wa.WA_ERR_INVALID_ARGUMENT
+    assert call(D=32) == wa.WA_ERR_UNSUPPORTED
+    assert call(vs=_S(wa, t=20 * 64 + 4)) == wa.WA_ERR_UNSUPPORTED
+    # the workspace holds two tensors' partials
+    one = wa.wa_kv_quant_fp8_workspace_size(2, 20, 1500, "tensor")
+    assert call(wsb=one) == wa.WA_ERR_WORKSPACE_TOO_SMALL
+
+
 def _dequant(wa, **kw):
     a = dict(cache=FAKE, cs=wa.Strides(20 * 1500 * 64, 64, 1500 * 64), L=1500, scale=FAKE, gran=0,
              fmt=0, lens=None, B=2, H=20, T=1500, D=64, x=FAKE, xs=_S(wa))

@@ -210,3 +210,59 @@ def test_dynamic_scale_long_rows_one_head(gpu):
     for gran in ("tensor", "head"):
         _assert_same(_run_quant(wa, x, lens, None, T, gran), _oracle(x, lens, None, T, gran),
                      f"long rows {gran}")
+
+
+def _run_pair(wa, k_cpu, v_cpu, lens, dst, L, gran, fmt, scales_in=None, k_dev=None):
+    B, T, H, D = k_cpu.shape
+    kd = k_dev if k_dev is not None else to_dev(k_cpu)
+    vd = to_dev(v_cpu)
+    kc = torch.full((B, H, L, D), GUARD, dtype=torch.uint8, device="cuda")
+    vc = torch.full_like(kc, GUARD)
+    n = 1 if gran == "tensor" else H
+    if scales_in is None:
+        ks = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        vs = torch.full_like(ks, float("nan"))
+    else:
+        ks, vs = (to_dev(np.asarray(x, dtype=np.float32)) for x in scales_in)
+    wa.wa_kv_quant_fp8_kv(kd, vd, kc, vc, ks, vs, gran, fmt,
+                          lens=None if lens is None else to_dev(np.asarray(lens, dtype=np.int32)),
+                          dst_start=None if dst is None else to_dev(np.asarray(dst, dtype=np.int32)),
+                          compute_scale=scales_in is None)
+    torch.cuda.synchronize()
+    return (kc.cpu().numpy(), ks.cpu().numpy()), (vc.cpu().numpy(), vs.cpu().numpy())
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("gran", ["tensor", "head"])
+def test_kv_pair_equals_two_fills(gpu, gran, fmt):
+    """wa_kv_quant_fp8_kv: K (a strided view) and V (contiguous) in one call,
+    each with its own scales, equal to two oracle fills; ragged lengths and
+    slots, some clipped."""
+    import whisper_attention_amd as wa
+    announce(f"quant K/V pair {gran} {fmt}")
+    B, T, H, L = 5, 40, 4, 64
+    base = workloads.bf16_normal((B, H, T, 64), 7, 83, 0.05, 20.0)
+    k_cpu = base.permute(0, 2, 1, 3)
+    k_dev = to_dev(base).permute(0, 2, 1, 3)
+    v_cpu = workloads.bf16_normal((B, T, H, 64), 7, 84, 0.0, 20.0) * 3
+    lens, dst = [40, 0, 1, 17, 40], [0, 5, 63, 30, 50]
+    got_k, got_v = _run_pair(wa, k_cpu, v_cpu, lens, dst, L, gran, fmt, k_dev=k_dev)
+    _assert_same(got_k, _oracle(k_cpu.contiguous(), lens, dst, L, gran, fmt=fmt), f"pair K {gran} {fmt}")
+    _assert_same(got_v, _oracle(v_cpu, lens, dst, L, gran, fmt=fmt), f"pair V {gran} {fmt}")
+
+
+def test_kv_pair_prefill_full_size_and_static_scales(gpu):
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["prefill"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    announce(f"quant K/V pair prefill B={B} H={H} T={T} per head, then static scales")
+    lens = workloads.lens_uniform(B, cfg["lo"], cfg["hi"], 0)
+    k = workloads.bf16_normal((B, T, H, 64), 0, workloads.TID_K, cfg["outlier_p"], cfg["outlier_mult"])
+    v = workloads.bf16_normal((B, T, H, 64), 0, workloads.TID_V, cfg["outlier_p"], cfg["outlier_mult"])
+    got_k, got_v = _run_pair(wa, k, v, lens, None, T, "head", "e4m3")
+    _assert_same(got_k, _oracle(k, lens, None, T, "head"), "pair prefill K")
+    _assert_same(got_v, _oracle(v, lens, None, T, "head"), "pair prefill V")
+    sk, sv = workloads.scales_uniform(H, 1, 85), workloads.scales_uniform(H, 1, 86)
+    got_k, got_v = _run_pair(wa, k, v, lens, None, T, "head", "e4m3", scales_in=(sk, sv))
+    _assert_same(got_k, _oracle(k, lens, None, T, "head", scale_in=sk), "pair static K")
+    _assert_same(got_v, _oracle(v, lens, None, T, "head", scale_in=sv), "pair static V")

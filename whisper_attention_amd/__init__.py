@@ -57,6 +57,8 @@ def _load():
     lib.wa_kv_quant_fp8.restype = I
     lib.wa_kv_quant_fp8_fmt.argtypes = [P, S, I, I, I, I, P, P, P, S, I, P, I, I, I, P, Z, P]
     lib.wa_kv_quant_fp8_fmt.restype = I
+    lib.wa_kv_quant_fp8_kv.argtypes = [P, S, P, S, I, I, I, I, P, P, P, P, S, I, P, P, I, I, I, P, Z, P]
+    lib.wa_kv_quant_fp8_kv.restype = I
     lib.wa_kv_dequant_fp8.argtypes = [P, S, I, P, I, I, P, I, I, I, I, P, S, P]
     lib.wa_kv_dequant_fp8.restype = I
     lib.wa_kv_quant_fp8_workspace_size.argtypes = [I, I, I, I]
@@ -78,7 +80,7 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_dequant_fp8",
+EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_quant_fp8_kv", "wa_kv_dequant_fp8",
             "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn", "wa_encoder_attn_fp8qk",
             "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
             "wa_status_string")
@@ -183,6 +185,32 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
                                    int(bool(compute_scale)), _ptr(workspace), ws_bytes,
                                    _stream(x, stream)))
     return scale
+
+
+def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3", lens=None,
+                       dst_start=None, compute_scale=True, workspace=None, stream=None):
+    """K and V [B][T][H][64] bf16 into their uint8 caches [B][H][L][64] (same
+    layout) and scales, in one call; see ``wa_kv_quant_fp8_fmt``."""
+    for t in (k, v):
+        _bits(t, torch.bfloat16)
+    for t in (k_cache, v_cache):
+        _bits(t, torch.uint8)
+    for t in (k_scale, v_scale):
+        _bits(t, torch.float32)
+    if k.shape != v.shape or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k/v and their caches must share shapes, and the caches their strides")
+    B, T, H, D = k.shape
+    g = _gran(gran)
+    if workspace is None and compute_scale:
+        n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=k.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.wa_kv_quant_fp8_kv(_ptr(k), _act_strides(k), _ptr(v), _act_strides(v), B, H, T, D,
+                                  _ptr(lens), _ptr(dst_start), _ptr(k_cache), _ptr(v_cache),
+                                  _cache_strides(k_cache), k_cache.shape[2], _ptr(k_scale), _ptr(v_scale),
+                                  g, _fmt(fmt), int(bool(compute_scale)), _ptr(workspace), ws_bytes,
+                                  _stream(k, stream)))
+    return k_scale, v_scale
 
 
 def wa_kv_dequant_fp8(cache, scale, gran, fmt, out=None, T_max=None, lens=None, stream=None):

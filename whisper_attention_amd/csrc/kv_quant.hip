@@ -76,14 +76,16 @@ __device__ __forceinline__ Lane lane_of(int P, int rows_per_pass) {
   return l;
 }
 
-__global__ __launch_bounds__(1024) void kv_amax_kernel(const uint16_t *__restrict__ x,
-                                                       wa_strides xs, int T_max, int P,
+// blockIdx.z picks the tensor (K or V of a pair call; 0 for one tensor).
+__global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_max, int P,
                                                        int rows_per_pass,
                                                        const int32_t *__restrict__ lens,
                                                        int per_head, int groups,
                                                        uint32_t *__restrict__ partial) {
   extern __shared__ uint32_t smax[];  // [groups]
   const int b = blockIdx.x;
+  const uint16_t *__restrict__ x = qt.x[blockIdx.z];
+  const wa_strides xs = qt.xs[blockIdx.z];
   const int rpp = max(rows_per_pass, 1);
   const int t0 = blockIdx.y * rpp * kAmaxLoads;
   const int t1 = min(t0 + rpp * kAmaxLoads, seq_len(lens, b, T_max));
@@ -114,16 +116,18 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(const uint16_t *__restric
     if (rows_per_pass > 0) break;
   }
   __syncthreads();
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) partial[(long)g * n_blocks + blk] = smax[g];
+  uint32_t *pz = partial + (long)blockIdx.z * groups * n_blocks;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) pz[(long)g * n_blocks + blk] = smax[g];
 }
 
-// One block per group: fold that group's n_blocks partials (contiguous).
+// One block per group (and tensor, blockIdx.z): fold that group's n_blocks
+// partials (contiguous).
 __global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restrict__ partial,
-                                                       int n_blocks, float fmax,
-                                                       float *__restrict__ scale) {
+                                                       int n_blocks, float fmax, QuantTensors qt) {
   __shared__ uint32_t wmax[4];
   const int g = blockIdx.x;
-  const uint32_t *pg = partial + (long)g * n_blocks;
+  float *__restrict__ scale = qt.scale[blockIdx.z];
+  const uint32_t *pg = partial + ((long)blockIdx.z * gridDim.x + g) * n_blocks;
   uint32_t m = 0;
   int j = threadIdx.x;
   for (; j + 768 < n_blocks; j += 1024) {
@@ -144,11 +148,13 @@ __global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restric
 
 template <Fp8 F>
 __global__ __launch_bounds__(1024) void kv_encode_kernel(
-    const uint16_t *__restrict__ x, wa_strides xs, int T_max, int P, int rows_per_pass,
-    const int32_t *__restrict__ lens, const int32_t *__restrict__ dst_start,
-    uint8_t *__restrict__ cache, wa_strides cs, int cache_len, const float *__restrict__ scale,
-    int per_head) {
+    QuantTensors qt, int T_max, int P, int rows_per_pass, const int32_t *__restrict__ lens,
+    const int32_t *__restrict__ dst_start, wa_strides cs, int cache_len, int per_head) {
   const int b = blockIdx.x;
+  const uint16_t *__restrict__ x = qt.x[blockIdx.z];
+  const wa_strides xs = qt.xs[blockIdx.z];
+  uint8_t *__restrict__ cache = qt.cache[blockIdx.z];
+  const float *__restrict__ scale = qt.scale[blockIdx.z];
   const int rpp = max(rows_per_pass, 1);
   const int t0 = blockIdx.y * rpp * kEncLoads;
   const int t1 = min(t0 + rpp * kEncLoads, seq_len(lens, b, T_max));
@@ -219,29 +225,28 @@ size_t quant_workspace_bytes(const QuantPlan &p) {
   return (n + 255) & ~(size_t)255;
 }
 
-hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
-                           const int32_t *lens, const int32_t *dst_start, uint8_t *cache,
-                           wa_strides cs, int cache_len, float *scale, int per_head,
-                           int compute_scale, Fp8 fmt, uint32_t *ws, const QuantPlan &plan,
-                           hipStream_t stream) {
+hipError_t launch_kv_quant(const QuantTensors &qt, int n_tensors, int B, int H, int T_max,
+                           const int32_t *lens, const int32_t *dst_start, wa_strides cs,
+                           int cache_len, int per_head, int compute_scale, Fp8 fmt, uint32_t *ws,
+                           const QuantPlan &plan, hipStream_t stream) {
   (void)H;
   if (compute_scale) {
     const size_t lds = (size_t)plan.groups * sizeof(uint32_t);
-    hipLaunchKernelGGL(kv_amax_kernel, dim3(B, plan.amax_chunks), dim3(plan.threads), lds, stream,
-                       x, xs, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, per_head,
+    hipLaunchKernelGGL(kv_amax_kernel, dim3(B, plan.amax_chunks, n_tensors), dim3(plan.threads), lds,
+                       stream, qt, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, per_head,
                        plan.groups, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float fmax = fmt == Fp8::E4M3 ? fp8_max<Fp8::E4M3>() : fp8_max<Fp8::E5M2>();
-    hipLaunchKernelGGL(kv_scale_kernel, dim3(plan.groups), dim3(256), 0, stream, ws,
-                       (int)plan.blocks, fmax, scale);
+    hipLaunchKernelGGL(kv_scale_kernel, dim3(plan.groups, 1, n_tensors), dim3(256), 0, stream, ws,
+                       (int)plan.blocks, fmax, qt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   auto kernel = fmt == Fp8::E4M3 ? kv_encode_kernel<Fp8::E4M3> : kv_encode_kernel<Fp8::E5M2>;
-  hipLaunchKernelGGL(kernel, dim3(B, plan.enc_chunks), dim3(plan.threads), 0, stream, x, xs, T_max,
-                     plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cache, cs, cache_len,
-                     scale, per_head);
+  hipLaunchKernelGGL(kernel, dim3(B, plan.enc_chunks, n_tensors), dim3(plan.threads), 0, stream, qt,
+                     T_max, plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cs, cache_len,
+                     per_head);
   return hipGetLastError();
 }
 

@@ -67,31 +67,68 @@ size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gra
   return wa::quant_workspace_bytes(wa::quant_plan(B, H, T_max, gran));
 }
 
-wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
-                              int head_dim, const int32_t *lens, const int32_t *dst_start,
-                              uint8_t *cache, wa_strides cs, int cache_len, float *scale,
-                              wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
-                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!x || !cache || !scale) return WA_ERR_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+
+// One tensor (v == nullptr) or a K/V pair sharing shape, lengths, slots and
+// cache layout.
+wa_status quant_common(const uint16_t *k, wa_strides ks, const uint16_t *v, wa_strides vs, int B,
+                       int H, int T_max, int head_dim, const int32_t *lens,
+                       const int32_t *dst_start, uint8_t *k_cache, uint8_t *v_cache,
+                       wa_strides cs, int cache_len, float *k_scale, float *v_scale,
+                       wa_scale_gran gran, wa_fp8_format fmt, int compute_scale, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const int n = v ? 2 : 1;
+  if (!k || !k_cache || !k_scale) return WA_ERR_INVALID_ARGUMENT;
+  if (n == 2 && (!v_cache || !v_scale)) return WA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || T_max <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
   if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
   if (fmt != WA_FP8_E4M3 && fmt != WA_FP8_E5M2) return WA_ERR_INVALID_ARGUMENT;
   if (compute_scale != 0 && compute_scale != 1) return WA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64) return WA_ERR_UNSUPPORTED;
   if (H > 8192 || T_max > 65535 * 8) return WA_ERR_UNSUPPORTED;
-  if (!bf16_layout_ok(x, xs) || !u8_layout_ok(cache, cs)) return WA_ERR_UNSUPPORTED;
+  if (!bf16_layout_ok(k, ks) || !u8_layout_ok(k_cache, cs)) return WA_ERR_UNSUPPORTED;
+  if (n == 2 && (!bf16_layout_ok(v, vs) || !u8_layout_ok(v_cache, cs))) return WA_ERR_UNSUPPORTED;
   const wa::QuantPlan plan = wa::quant_plan(B, H, T_max, gran);
   if (compute_scale) {
     if (!workspace) return WA_ERR_INVALID_ARGUMENT;
     if (!aligned16(workspace)) return WA_ERR_UNSUPPORTED;
-    if (workspace_bytes < wa::quant_workspace_bytes(plan)) return WA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < n * wa::quant_workspace_bytes(plan)) return WA_ERR_WORKSPACE_TOO_SMALL;
   }
   wa_status st = check_device();
   if (st != WA_OK) return st;
-  return from_hip(wa::launch_kv_quant(x, xs, B, H, T_max, lens, dst_start, cache, cs, cache_len,
-                                      scale, gran == WA_SCALE_PER_HEAD, compute_scale,
+  wa::QuantTensors qt = {{k, v}, {ks, vs}, {k_cache, v_cache}, {k_scale, v_scale}};
+  return from_hip(wa::launch_kv_quant(qt, n, B, H, T_max, lens, dst_start, cs, cache_len,
+                                      gran == WA_SCALE_PER_HEAD, compute_scale,
                                       fmt == WA_FP8_E4M3 ? wa::Fp8::E4M3 : wa::Fp8::E5M2,
                                       static_cast<uint32_t *>(workspace), plan, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
+                              int head_dim, const int32_t *lens, const int32_t *dst_start,
+                              uint8_t *cache, wa_strides cs, int cache_len, float *scale,
+                              wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return quant_common(x, xs, nullptr, wa_strides{0, 0, 0}, B, H, T_max, head_dim, lens, dst_start,
+                      cache, nullptr, cs, cache_len, scale, nullptr, gran, fmt, compute_scale,
+                      workspace, workspace_bytes, stream);
+}
+
+wa_status wa_kv_quant_fp8_kv(const uint16_t *k, wa_strides ks, const uint16_t *v, wa_strides vs,
+                             int B, int H, int T_max, int head_dim, const int32_t *lens,
+                             const int32_t *dst_start, uint8_t *k_cache, uint8_t *v_cache,
+                             wa_strides cs, int cache_len, float *k_scale, float *v_scale,
+                             wa_scale_gran gran, wa_fp8_format fmt, int compute_scale,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!v) return WA_ERR_INVALID_ARGUMENT;
+  return quant_common(k, ks, v, vs, B, H, T_max, head_dim, lens, dst_start, k_cache, v_cache, cs,
+                      cache_len, k_scale, v_scale, gran, fmt, compute_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,

@@ -24,11 +24,19 @@ struct QuantPlan {
 QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran);
 size_t quant_workspace_bytes(const QuantPlan &p);
 
-hipError_t launch_kv_quant(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
-                           const int32_t *lens, const int32_t *dst_start, uint8_t *cache,
-                           wa_strides cs, int cache_len, float *scale, int per_head,
-                           int compute_scale, Fp8 fmt, uint32_t *ws, const QuantPlan &plan,
-                           hipStream_t stream);
+// One or two tensors (K and V) that share shape, lengths, slots and the cache
+// layout; each has its own input, cache and scales.
+struct QuantTensors {
+  const uint16_t *x[2];
+  wa_strides xs[2];
+  uint8_t *cache[2];
+  float *scale[2];
+};
+// The workspace holds n_tensors * quant_workspace_bytes(plan) bytes.
+hipError_t launch_kv_quant(const QuantTensors &qt, int n_tensors, int B, int H, int T_max,
+                           const int32_t *lens, const int32_t *dst_start, wa_strides cs,
+                           int cache_len, int per_head, int compute_scale, Fp8 fmt, uint32_t *ws,
+                           const QuantPlan &plan, hipStream_t stream);
 
 // ---- dequantize -----------------------------------------------------------
 hipError_t launch_kv_dequant(const uint8_t *cache, wa_strides cs, int cache_len, const float *scale,
