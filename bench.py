@@ -40,23 +40,33 @@ N_SETS = 3                    # decode cache sets used in turn
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled
 # by what the counter reads for a plain 256 MiB copy (the commands and raw
-# counts are in profiles/hbm_traffic_counters.md), with the sha256 prefix of
-# the kernel source they were taken on: a changed kernel reports null.
+# counts are in profiles/hbm_traffic_counters.md), with the code hash (see
+# code_hash) of the kernel source they were taken on: a changed kernel
+# reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("91473fdc834d89e4", {"encoder": 251.98e6, "prefill": 148.25e6,
+    "encoder_attn.hip": ("24fa7ac9fb1bab47", {"encoder": 251.98e6, "prefill": 148.25e6,
                                               "fp8qk_30s": 190.51e6}),
-    "decode_attn.hip": ("bf7c58da424c2f68", {"cross": 246.21e6, "self": 42.13e6}),
-    "kv_dequant.hip": ("b81e378329bb8a7d", {"cross": 368.69e6}),
+    "decode_attn.hip": ("90acdc967b200294", {"cross": 246.21e6, "self": 42.13e6}),
+    "kv_dequant.hip": ("63eef794f2b6b3a5", {"cross": 368.69e6}),
 }
 
 
-def traffic(source, launch):
+def code_hash(path):
+    """sha256 prefix of a source with its comments and blank space removed, so
+    that an edit of the comments alone keeps the counters that were taken."""
     import hashlib
+    import re
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
+
+
+def traffic(source, launch):
     sha, values = TRAFFIC[source]
-    path = os.path.join(ROOT, "whisper_attention_amd", "csrc", source)
-    with open(path, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
-            return None
+    if code_hash(os.path.join(ROOT, "whisper_attention_amd", "csrc", source)) != sha:
+        return None
     return values[launch]
 
 

@@ -451,9 +451,9 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], cons
     float alpha[2];
     if (tile_max<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, alpha))
       rescale(st, alpha, x.lane);
-    // The exponentials go to the transcendental unit at a quarter of the FMA
-    // rate; the scheduling groups interleave them with the FMAs and
-    // conversions, which then issue in their shadow instead of before them.
+    // An exponential costs two to four times the issue time of an FMA; the
+    // scheduling groups interleave them with the FMAs and conversions,
+    // which then issue in their shadow instead of before them.
     softmax_exp(s, st.m_run, x.c_log2, pa);
 #pragma unroll
     for (int g = 0; g < 64; ++g) {
