@@ -553,7 +553,7 @@ def main():
         "encoder_fp8qk": enc_fp8,
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false> (encoder)",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false, false> (encoder)",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic("encoder_attn.hip", "encoder"), "traffic_unit": "bytes per launch",
