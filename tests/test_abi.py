@@ -249,3 +249,22 @@ def test_decode_append_validation(wa):
     assert _app(wa, ns=wa.Strides(20 * 64, 0, 12)) == wa.WA_ERR_UNSUPPORTED
     assert _app(wa, ws=None) == wa.WA_ERR_INVALID_ARGUMENT
     assert _app(wa, wsb=64) == wa.WA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_refuses_host_tensors_and_bad_vectors(wa):
+    """The binding passes only device pointers: host tensors are refused
+    before any library call (the kernels would dereference them on the GPU)."""
+    import torch
+    q = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wa.wa_encoder_attn(q, q, q, out=torch.empty_like(q))
+    c = torch.zeros((1, 2, 4, 64), dtype=torch.uint8)
+    s = torch.ones(1, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        wa.wa_decode_attn(torch.zeros((1, 2, 64), dtype=torch.bfloat16), c, c, s, s,
+                          torch.ones(1, dtype=torch.int32), "tensor", workspace=torch.zeros(16, dtype=torch.uint8))
+    # a vector of the wrong dtype or length is refused whatever its device
+    with pytest.raises(ValueError, match="lens"):
+        wa._vec(torch.ones(3, dtype=torch.int64), torch.int32, 3, "lens")
+    with pytest.raises(ValueError, match="scale"):
+        wa._vec(torch.ones(2, dtype=torch.float32), torch.float32, 20, "scale")

@@ -112,7 +112,23 @@ def _fmt(f):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a GPU tensor (None passes through).  The kernels
+    dereference every pointer on the device, so a host tensor is refused."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor (the library reads every buffer on the device)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _vec(t, dtype, n, what):
+    """A contiguous device vector of at least n elements (lengths, slots, scales)."""
+    if t is None:
+        return None
+    if t.dtype != dtype or t.dim() != 1 or t.numel() < n or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous {dtype} vector of at least {n} elements, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    return _ptr(t)
 
 
 def _stream(t, stream):
@@ -179,9 +195,11 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
         n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.wa_kv_quant_fp8_fmt(_ptr(x), _act_strides(x), B, H, T, D, _ptr(lens),
-                                   _ptr(dst_start), _ptr(cache), _cache_strides(cache),
-                                   cache.shape[2], _ptr(scale), g, _fmt(fmt),
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
+    _check(lib.wa_kv_quant_fp8_fmt(_ptr(x), _act_strides(x), B, H, T, D, _vec(lens, torch.int32, B, "lens"),
+                                   _vec(dst_start, torch.int32, B, "dst_start"), _ptr(cache),
+                                   _cache_strides(cache), cache.shape[2],
+                                   _vec(scale, torch.float32, ng, "scale"), g, _fmt(fmt),
                                    int(bool(compute_scale)), _ptr(workspace), ws_bytes,
                                    _stream(x, stream)))
     return scale
@@ -205,9 +223,12 @@ def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3
         n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_kv_quant_fp8_kv(_ptr(k), _act_strides(k), _ptr(v), _act_strides(v), B, H, T, D,
-                                  _ptr(lens), _ptr(dst_start), _ptr(k_cache), _ptr(v_cache),
-                                  _cache_strides(k_cache), k_cache.shape[2], _ptr(k_scale), _ptr(v_scale),
+                                  _vec(lens, torch.int32, B, "lens"), _vec(dst_start, torch.int32, B, "dst_start"),
+                                  _ptr(k_cache), _ptr(v_cache), _cache_strides(k_cache), k_cache.shape[2],
+                                  _vec(k_scale, torch.float32, ng, "k_scale"),
+                                  _vec(v_scale, torch.float32, ng, "v_scale"),
                                   g, _fmt(fmt), int(bool(compute_scale)), _ptr(workspace), ws_bytes,
                                   _stream(k, stream)))
     return k_scale, v_scale
@@ -227,8 +248,11 @@ def wa_kv_dequant_fp8(cache, scale, gran, fmt, out=None, T_max=None, lens=None, 
     if out.dim() != 4 or (out.shape[0], out.shape[2], out.shape[3]) != (B, H, D):
         raise ValueError(f"out must be [B={B}][T][H={H}][{D}], got {tuple(out.shape)}")
     T = out.shape[1]
-    _check(lib.wa_kv_dequant_fp8(_ptr(cache), _cache_strides(cache), L, _ptr(scale), _gran(gran),
-                                 _fmt(fmt), _ptr(lens), B, H, T, D, _ptr(out), _act_strides(out),
+    g = _gran(gran)
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
+    _check(lib.wa_kv_dequant_fp8(_ptr(cache), _cache_strides(cache), L, _vec(scale, torch.float32, ng, "scale"),
+                                 g, _fmt(fmt), _vec(lens, torch.int32, B, "lens"), B, H, T, D, _ptr(out),
+                                 _act_strides(out),
                                  _stream(cache, stream)))
     return out
 
@@ -242,7 +266,7 @@ def wa_encoder_attn(q, k, v, out=None, lens=None, causal=False, softmax_scale=0.
         out = torch.empty_like(q)
     _check(lib.wa_encoder_attn(_ptr(q), _act_strides(q), _ptr(k), _act_strides(k), _ptr(v),
                                _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
-                               _ptr(lens), int(bool(causal)), float(softmax_scale),
+                               _vec(lens, torch.int32, B, "lens"), int(bool(causal)), float(softmax_scale),
                                _stream(q, stream)))
     return out
 
@@ -261,9 +285,12 @@ def wa_encoder_attn_fp8qk(q, q_scale, k, k_scale, gran, v, out=None, lens=None, 
         raise ValueError("q, k and v must share the [B][T][H][64] shape")
     if out is None:
         out = torch.empty_like(v)
-    _check(lib.wa_encoder_attn_fp8qk(_ptr(q), _act_strides(q), _ptr(q_scale), _ptr(k), _act_strides(k),
-                                     _ptr(k_scale), _gran(gran), _ptr(v), _act_strides(v), _ptr(out),
-                                     _act_strides(out), B, H, T, D, _ptr(lens), int(bool(causal)),
+    g = _gran(gran)
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
+    _check(lib.wa_encoder_attn_fp8qk(_ptr(q), _act_strides(q), _vec(q_scale, torch.float32, ng, "q_scale"),
+                                     _ptr(k), _act_strides(k), _vec(k_scale, torch.float32, ng, "k_scale"),
+                                     g, _ptr(v), _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
+                                     _vec(lens, torch.int32, B, "lens"), int(bool(causal)),
                                      float(softmax_scale), _stream(v, stream)))
     return out
 
@@ -284,9 +311,12 @@ def wa_decode_attn(q, k_cache, v_cache, k_scale, v_scale, lens, gran, softmax_sc
         n = wa_decode_attn_workspace_size(B, H, L)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    g = _gran(gran)
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_decode_attn(_ptr(q), _tok_strides(q), _ptr(k_cache), _ptr(v_cache),
-                              _cache_strides(k_cache), L, _ptr(k_scale), _ptr(v_scale),
-                              _gran(gran), _ptr(lens), B, H, D, float(softmax_scale), _ptr(out),
+                              _cache_strides(k_cache), L, _vec(k_scale, torch.float32, ng, "k_scale"),
+                              _vec(v_scale, torch.float32, ng, "v_scale"), g,
+                              _vec(lens, torch.int32, B, "lens"), B, H, D, float(softmax_scale), _ptr(out),
                               _tok_strides(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
     return out
 
@@ -312,10 +342,13 @@ def wa_decode_attn_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, l
         n = wa_decode_attn_workspace_size(B, H, L)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    g = _gran(gran)
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_decode_attn_append(_ptr(q), _tok_strides(q), _ptr(k_new), _ptr(v_new),
                                      _tok_strides(k_new), _ptr(k_cache), _ptr(v_cache),
-                                     _cache_strides(k_cache), L, _ptr(k_scale), _ptr(v_scale),
-                                     _gran(gran), _ptr(lens), B, H, D, float(softmax_scale),
+                                     _cache_strides(k_cache), L, _vec(k_scale, torch.float32, ng, "k_scale"),
+                                     _vec(v_scale, torch.float32, ng, "v_scale"), g,
+                                     _vec(lens, torch.int32, B, "lens"), B, H, D, float(softmax_scale),
                                      _ptr(out), _tok_strides(out), _ptr(workspace), ws_bytes,
                                      _stream(q, stream)))
     return out
