@@ -60,6 +60,41 @@ def dense_attention(q, k, v, lens, causal, softmax_scale, with_magnitude=False):
     return (out, mag) if with_magnitude else out
 
 
+def cross_attention(q, k, v, q_lens, k_lens, softmax_scale, with_magnitude=False):
+    """Decoder cross-attention with a multi-token query (a prompt attending to
+    the encoded audio): whisper-blaze's decoder_cross_attn, "no causal mask"
+    (PyPI page, "Direct Kernel API"), with the query and the keys of
+    different lengths ("Unlocking the power of OpenAI's Whisper", section 3:
+    the decoder attends over the encoder's output).
+
+    q: [B][Tq][H][D]; k, v: [B][Tk][H][D].  Query row i < q_lens[b] attends
+    to every key j < k_lens[b]; other rows are NaN, and a row with no key
+    (k_lens[b] = 0) is zero.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Tq, H, D = q.shape
+    out = np.full((B, Tq, H, D), np.nan, dtype=np.float64)
+    mag = np.full((B, Tq, H, D), np.nan, dtype=np.float64) if with_magnitude else None
+    for b in range(B):
+        nq, nk = int(q_lens[b]), int(k_lens[b])
+        if nq == 0:
+            continue
+        if nk == 0:
+            out[b, :nq] = 0.0
+            if with_magnitude:
+                mag[b, :nq] = 0.0
+            continue
+        for h in range(H):
+            s = softmax_scale * (q[b, :nq, h, :] @ k[b, :nk, h, :].T)   # [nq][nk]
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[b, :nq, h, :] = (p @ v[b, :nk, h, :]) / p.sum(axis=1, keepdims=True)
+            if with_magnitude:
+                mag[b, :nq, h, :] = (p @ np.abs(v[b, :nk, h, :])) / p.sum(axis=1, keepdims=True)
+    return (out, mag) if with_magnitude else out
+
+
 def dense_attention_fp8qk(q_codes, q_scale, k_codes, k_scale, gran, v, lens, causal, softmax_scale,
                           with_magnitude=False):
     """Dense attention with Q and K given as E4M3 codes and dequantization scales.

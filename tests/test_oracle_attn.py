@@ -239,3 +239,40 @@ def test_fp8qk_scale_moves_between_q_and_k_and_softmax_scale():
     b = attn.dense_attention_fp8qk(qc, np.float32([0.04]), kc, np.float32([0.02]), quant.PER_TENSOR, v,
                                    [7], False, 0.0625)
     np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+def test_cross_attention_brute_force_ragged():
+    """Pure-Python loops: query rows below q_lens attend to keys below k_lens."""
+    g = np.random.default_rng(31)
+    B, Tq, Tk, H, D = 3, 5, 9, 2, 4
+    q = g.standard_normal((B, Tq, H, D))
+    k = g.standard_normal((B, Tk, H, D))
+    v = g.standard_normal((B, Tk, H, D))
+    ql, kl = [5, 2, 0], [9, 1, 4]
+    got = attn.cross_attention(q, k, v, ql, kl, 0.3)
+    for b in range(B):
+        assert np.all(np.isnan(got[b, ql[b]:]))
+        for h in range(H):
+            for i in range(ql[b]):
+                s = [0.3 * sum(q[b, i, h, d] * k[b, j, h, d] for d in range(D)) for j in range(kl[b])]
+                w = [math.exp(x - max(s)) for x in s]
+                want = [sum(w[j] * v[b, j, h, d] for j in range(kl[b])) / sum(w) for d in range(D)]
+                np.testing.assert_allclose(got[b, i, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_cross_attention_special_cases():
+    g = np.random.default_rng(32)
+    B, T, H, D = 2, 11, 3, 64
+    q, k, v = (g.standard_normal((B, T, H, D)) for _ in range(3))
+    lens = np.array([11, 6])
+    # equal query and key lengths: the non-causal dense attention
+    np.testing.assert_allclose(attn.cross_attention(q, k, v, lens, lens, 0.125),
+                               attn.dense_attention(q, k, v, lens, False, 0.125), rtol=1e-12, equal_nan=True)
+    # no keys: zero rows
+    z = attn.cross_attention(q, k, v, [3, 0], [0, 5], 0.125)
+    assert np.all(z[0, :3] == 0) and np.all(np.isnan(z[0, 3:])) and np.all(np.isnan(z[1]))
+    # one query row: the decode attention over the same (unquantized) keys
+    one = attn.cross_attention(q[:, :1], k, v, [1, 1], lens, 0.125)
+    dec = attn.decode_attention_dequant(q[:, 0], np.transpose(k, (0, 2, 1, 3)), np.transpose(v, (0, 2, 1, 3)),
+                                        lens, 0.125)
+    np.testing.assert_allclose(one[:, 0], dec, rtol=1e-12)
