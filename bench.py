@@ -16,9 +16,11 @@ algorithmic flops per call over the call's average duration, measured with
 HIP events on the launch stream); the decode throughput in GB/s (algorithmic
 bytes: every cached K/V byte read once plus q and o) sits beside it, each
 with its fraction of the MI355X peak.  ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the encoder workload.
+on a bounded sample of the encoder workload.  Before the W warmup steps,
+untimed steps run for --settle-ms (100 ms) while the GPU's clocks rise from
+idle; the JSON line records how many (settle_steps).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--settle-ms MS] [--gpus 1] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -73,8 +75,11 @@ def traffic(source, launch):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the warmup, run untimed steps for this long: the GPU's clocks take "
+                         "about 40 ms of back-to-back steps to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -380,6 +385,38 @@ def encoder_windows(steps, g_seed):
     return res
 
 
+def cross_prefill(steps, g_seed):
+    """Prompt-prefill cross-attention (wa_cross_attn): B=128 prompts of
+    U[4,224] tokens, 20 heads, against 1500 encoder frames of bf16 K/V.
+    TFLOP/s counts the valid rows only, 4*H*1500*64*sum(lens)."""
+    import workloads
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["prefill_cross"]
+    B, H, Tq, Tk = cfg["B"], cfg["H"], cfg["T"], cfg["T_k"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    q = gen_bf16((B, Tq, H, HEAD_DIM), g)
+    k, v = (gen_bf16((B, Tk, H, HEAD_DIM), g, cfg["outlier_p"]) for _ in range(2))
+    lens_np = workloads.lens_uniform(B, cfg["lo"], cfg["hi"], g_seed)
+    lens = torch.from_numpy(lens_np).cuda()
+    o = torch.empty_like(q)
+    for _ in range(3):
+        wa.wa_cross_attn(q, k, v, out=o, q_lens=lens)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        wa.wa_cross_attn(q, k, v, out=o, q_lens=lens)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    tf = 4.0 * H * Tk * HEAD_DIM * float(lens_np.sum()) / (us * 1e-6) / 1e12
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+           "us": round(us, 2), "B": B, "H": H, "T_q": Tq, "T_k": Tk, "q_lens": f"U[{cfg['lo']},{cfg['hi']}]",
+           "mean_q_len": round(float(lens_np.mean()), 1)}
+    del q, k, v, o
+    return res
+
+
 def encoder_fp8qk(steps, g_seed):
     """The encoder with E4M3 Q and K (wa_encoder_attn_fp8qk, per-tensor
     scales) at the 30-s, 15-s and 10-s windows.  The codes are written once,
@@ -459,6 +496,12 @@ def main():
         sys.exit(1)
     print(f"[bench] setting up inputs (steps={args.steps} warmup={args.warmup})", file=sys.stderr, flush=True)
     wl = Workload(seed=0)
+    t_settle, n_settle = time.perf_counter(), 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        wl.run(n_settle)
+        n_settle += 1
+        if n_settle % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         wl.run(i)
     torch.cuda.synchronize()
@@ -488,6 +531,7 @@ def main():
     dms = dseg.mean(axis=0)
     windows = encoder_windows(args.steps, g_seed=1)
     enc_fp8 = encoder_fp8qk(args.steps, g_seed=3)
+    xpre = cross_prefill(args.steps, g_seed=4)
     graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
     codecs = codec_rates(wl, args.steps)
     if args.copy_calib:
@@ -517,6 +561,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -553,6 +598,7 @@ def main():
         "encoder_fp8qk": enc_fp8,
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
+        "prefill_cross_attn": xpre,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false, false> (encoder)",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),

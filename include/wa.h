@@ -196,9 +196,9 @@ wa_status wa_kv_dequant_fp8(const uint8_t *cache, wa_strides cs, int cache_len,
  *
  * What: per sequence b, head h and query i < lens[b]:
  *     O[i] = sum_j softmax_j(softmax_scale * Q[i] . K[j]) V[j]
- *   over keys j < lens[b] (causal = 0: encoder self-attention, "no causal
- *   mask" in whisper-blaze "Direct Kernel API") or j <= i (causal = 1:
- *   decoder prompt prefill, the "causal mask" of decoder_self_attn).
+ *   over keys j < lens[b] (causal = 0: encoder self-attention, unmasked in
+ *   whisper-blaze "Direct Kernel API") or j <= i (causal = 1: decoder prompt
+ *   prefill, masked causally as decoder_self_attn is there).
  *   Accumulation is fp32; O is written as bf16 (round to nearest even).
  *   Rows i >= lens[b] of O are not written.
  *
@@ -212,6 +212,37 @@ wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, w
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
                           int H, int T_max, int head_dim, const int32_t *lens, int causal,
                           float softmax_scale, hipStream_t stream);
+
+/*
+ * wa_cross_attn -- decoder cross-attention for a block of query tokens.
+ *
+ * What: whisper-blaze's decoder_cross_attn (PyPI page, "Direct Kernel API":
+ *   no mask) for several decoder tokens at once, such as a prompt attending to
+ *   the encoder's output ("Unlocking the power of OpenAI's Whisper", section
+ *   3: the decoder attends over the encoded audio).  Per sequence b and head h,
+ *   for query i < q_lens[b]:
+ *     O[i] = sum_{j < k_lens[b]} softmax_j(softmax_scale * Q[i] . K[j]) V[j]
+ *   with fp32 accumulation, O written as bf16 (round to nearest even).  Rows
+ *   i >= q_lens[b] are not written; k_lens[b] = 0 gives zero rows.  With
+ *   T_q = T_k and q_lens = k_lens this is wa_encoder_attn with causal = 0.
+ *   K and V may be any [B][T_k][H][64] view, e.g. a [B][H][T_k][64] bf16
+ *   cache (ks.t = 64, ks.h = T_k * 64); a float8 cache is first expanded with
+ *   wa_kv_dequant_fp8.
+ *
+ * q, o       device bf16 [B][T_q][H][64] with strides qs, os; o must not alias
+ *            q, k or v.
+ * k, v       device bf16 [B][T_k][H][64] with strides ks, vs.
+ * q_lens     device int32 [B] or NULL (= T_q); values clamped to [0, T_q].
+ * k_lens     device int32 [B] or NULL (= T_k); values clamped to [0, T_k].
+ * Errors: null tensor pointer, non-positive B, H, T_q or T_k, or a
+ *   softmax_scale that is not finite and positive -> WA_ERR_INVALID_ARGUMENT;
+ *   head_dim != 64, layout (16-byte alignment, strides multiples of 8),
+ *   ks.t or vs.t of 2^24 or more -> WA_ERR_UNSUPPORTED.
+ */
+wa_status wa_cross_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+                        const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B, int H,
+                        int T_q, int T_k, int head_dim, const int32_t *q_lens,
+                        const int32_t *k_lens, float softmax_scale, hipStream_t stream);
 
 /*
  * wa_encoder_attn_fp8qk -- wa_encoder_attn with Q and K given in float8 E4M3.

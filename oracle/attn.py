@@ -62,7 +62,7 @@ def dense_attention(q, k, v, lens, causal, softmax_scale, with_magnitude=False):
 
 def cross_attention(q, k, v, q_lens, k_lens, softmax_scale, with_magnitude=False):
     """Decoder cross-attention with a multi-token query (a prompt attending to
-    the encoded audio): whisper-blaze's decoder_cross_attn, "no causal mask"
+    the encoded audio): whisper-blaze's decoder_cross_attn, which masks nothing
     (PyPI page, "Direct Kernel API"), with the query and the keys of
     different lengths ("Unlocking the power of OpenAI's Whisper", section 3:
     the decoder attends over the encoder's output).

@@ -173,6 +173,30 @@ def test_encoder_validation(wa):
     assert _enc(wa, ks=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
 
 
+def _cross(wa, **kw):
+    s = _S(wa)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, qs=s, ks=s, vs=s, os=s, B=2, H=20, Tq=224, Tk=1500, D=64,
+             ql=None, kl=None, sc=0.125)
+    a.update(kw)
+    return wa.lib.wa_cross_attn(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"],
+                                a["B"], a["H"], a["Tq"], a["Tk"], a["D"], a["ql"], a["kl"], a["sc"], None)
+
+
+def test_cross_validation(wa):
+    for name in ("q", "k", "v", "o"):
+        assert _cross(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    for name in ("B", "H", "Tq", "Tk"):
+        assert _cross(wa, **{name: 0}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _cross(wa, sc=float("inf")) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _cross(wa, sc=-0.125) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _cross(wa, D=32) == wa.WA_ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "o"):
+        assert _cross(wa, **{name: MIS}) == wa.WA_ERR_UNSUPPORTED
+    assert _cross(wa, qs=_S(wa, b=4)) == wa.WA_ERR_UNSUPPORTED
+    assert _cross(wa, ks=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
+    assert _cross(wa, vs=_S(wa, t=1 << 24)) == wa.WA_ERR_UNSUPPORTED
+
+
 def _enc8(wa, **kw):
     s = _S(wa)
     a = dict(q=FAKE, qs=s, qsc=FAKE, k=FAKE, ks=s, ksc=FAKE, gran=0, v=FAKE, vs=s, o=FAKE, os=s, B=2, H=20,
@@ -227,6 +251,7 @@ def test_valid_call_without_device_reports_hip_error(wa):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible: a valid call with fake pointers would launch")
     assert _enc(wa) == wa.WA_ERR_HIP
+    assert _cross(wa) == wa.WA_ERR_HIP
 
 
 def _app(wa, **kw):
@@ -258,6 +283,10 @@ def test_binding_refuses_host_tensors_and_bad_vectors(wa):
     q = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         wa.wa_encoder_attn(q, q, q, out=torch.empty_like(q))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wa.wa_cross_attn(q, q, q)
+    with pytest.raises(ValueError, match="k and v"):
+        wa.wa_cross_attn(q, q[:, :, :1], q)
     c = torch.zeros((1, 2, 4, 64), dtype=torch.uint8)
     s = torch.ones(1, dtype=torch.float32)
     with pytest.raises(ValueError):

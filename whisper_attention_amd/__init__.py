@@ -9,6 +9,8 @@ The functions keep the C names:
 * ``wa_kv_dequant_fp8``  float8 cache -> bf16
 * ``wa_encoder_attn``  dense bf16 attention (encoder, or causal prompt prefill)
   (``wa_encoder_attn_fp8qk``: E4M3 Q and K)
+* ``wa_cross_attn``    decoder cross-attention for several query tokens (query
+  and key lengths differ)
 * ``wa_decode_attn``   one query token per sequence against an E4M3 cache
 
 The library must have been built (``python whisper_attention_amd/build.py``);
@@ -67,6 +69,8 @@ def _load():
     lib.wa_encoder_attn.restype = I
     lib.wa_encoder_attn_fp8qk.argtypes = [P, S, P, P, S, P, I, P, S, P, S, I, I, I, I, P, I, F, P]
     lib.wa_encoder_attn_fp8qk.restype = I
+    lib.wa_cross_attn.argtypes = [P, S, P, S, P, S, P, S, I, I, I, I, I, P, P, F, P]
+    lib.wa_cross_attn.restype = I
     lib.wa_decode_attn.argtypes = [P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
     lib.wa_decode_attn.restype = I
     lib.wa_decode_attn_append.argtypes = [P, S, P, P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
@@ -82,7 +86,7 @@ lib = _load()
 
 EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_quant_fp8_kv", "wa_kv_dequant_fp8",
             "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn", "wa_encoder_attn_fp8qk",
-            "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
+            "wa_cross_attn", "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
             "wa_status_string")
 
 
@@ -292,6 +296,24 @@ def wa_encoder_attn_fp8qk(q, q_scale, k, k_scale, gran, v, out=None, lens=None, 
                                      g, _ptr(v), _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
                                      _vec(lens, torch.int32, B, "lens"), int(bool(causal)),
                                      float(softmax_scale), _stream(v, stream)))
+    return out
+
+
+def wa_cross_attn(q, k, v, out=None, q_lens=None, k_lens=None, softmax_scale=0.125, stream=None):
+    """Cross-attention of bf16 queries [B][Tq][H][64] over bf16 keys and
+    values [B][Tk][H][64] (any strided views); returns ``out``."""
+    for t in (q, k, v):
+        _bits(t, torch.bfloat16)
+    B, Tq, H, D = q.shape
+    Tk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must be [B][Tk][H][64] with q's B, H and head size")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.wa_cross_attn(_ptr(q), _act_strides(q), _ptr(k), _act_strides(k), _ptr(v),
+                             _act_strides(v), _ptr(out), _act_strides(out), B, H, Tq, Tk, D,
+                             _vec(q_lens, torch.int32, B, "q_lens"), _vec(k_lens, torch.int32, B, "k_lens"),
+                             float(softmax_scale), _stream(q, stream)))
     return out
 
 

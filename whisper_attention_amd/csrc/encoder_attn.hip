@@ -463,14 +463,26 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], cons
   }
 }
 
+// Rows i < len_q of o for a sequence with no key: the empty sum is zero.
+__device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int h, int q0, int len_q) {
+  const int i = q0 + (int)threadIdx.x;
+  if (i >= len_q) return;
+  uint4 *op = reinterpret_cast<uint4 *>(o + (long)b * os.b + (long)i * os.t + (long)h * os.h);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) op[c] = uint4{0u, 0u, 0u, 0u};
+}
+
 // kFp8: q and k hold E4M3 codes (uint8, strides in bytes) with
 // dequantization scales q_scale / k_scale ([1], or [H] when per_head).
+// Queries i < q_lens[b] (of Tq_max rows) attend keys j < k_lens[b] (of Tk_max
+// rows); the causal form needs both to be the same sequence.
 template <bool kCausal, bool kFp8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
     const void *__restrict__ q, wa_strides qs, const void *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
-    int T_max, const int32_t *__restrict__ lens, float c_log2, const float *__restrict__ q_scale,
-    const float *__restrict__ k_scale, int per_head, int n_qt, int total) {
+    int Tq_max, const int32_t *__restrict__ q_lens, int Tk_max, const int32_t *__restrict__ k_lens,
+    float c_log2, const float *__restrict__ q_scale, const float *__restrict__ k_scale, int per_head,
+    int n_qt, int total) {
   // XCD-aware order: blocks are dispatched round robin over the 8 XCDs, so
   // block L runs on XCD L % 8.  Give each XCD a contiguous run of work items
   // so the query tiles of one (b, h) share that XCD's L2 copy of K and V.
@@ -481,9 +493,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   int qt = item - bh * n_qt;
   if (kCausal) qt = n_qt - 1 - qt;  // longest rows first
   const int b = bh / H, h = bh - b * H;
-  const int len = min(max(lens ? lens[b] : T_max, 0), T_max);
+  const int len = min(max(q_lens ? q_lens[b] : Tq_max, 0), Tq_max);
   const int q0 = qt * kBM;
   if (q0 >= len) return;
+  const int len_k = min(max(k_lens ? k_lens[b] : Tk_max, 0), Tk_max);
+  if (len_k == 0) {
+    zero_rows(o, os, b, h, q0, len);
+    return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -493,9 +510,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   x.vp = v + (long)b * vs.b + (long)h * vs.h;
   x.ks = ks;
   x.vs = vs;
-  x.kend = kCausal ? min(len, q0 + kBM) : len;
+  x.kend = kCausal ? min(len_k, q0 + kBM) : len_k;
   x.nt = (x.kend + kBN - 1) / kBN;
-  x.len = len;
+  x.len = len_k;
   x.wq_lo = q0 + w * kQW;
   x.lane = lane;
   x.w = w;
@@ -508,6 +525,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   issue_tile<kFp8>(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
   if (x.nt > 1) issue_tile<kFp8>(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, x.k8, lane, w);
   x.ro = read_offsets(lane);
+  if (x.wq_lo >= len) {
+    // Every query of this wave lies past the query length (short prompts in
+    // a 256-row tile): it does its share of the copies and passes the same
+    // barriers as the other waves, and computes nothing.
+    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8>((t + 2) & 3, t, x);
+    return;
+  }
 
   WaveState st;
 #pragma unroll
@@ -582,17 +606,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 
 hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_strides ks,
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
-                          int H, int T_max, const int32_t *lens, int causal, float softmax_scale,
+                          int H, int Tq_max, const int32_t *q_lens, int Tk_max,
+                          const int32_t *k_lens, int causal, float softmax_scale,
                           const float *q_scale, const float *k_scale, int per_head, hipStream_t stream) {
   const float c_log2 = softmax_scale * kLog2e;
-  const int n_qt = (T_max + kBM - 1) / kBM;
+  const int n_qt = (Tq_max + kBM - 1) / kBM;
   const long total = (long)B * H * n_qt;
   const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(kWaves * 64);
   const bool fp8 = q_scale != nullptr;
   auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
                        : (fp8 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H, T_max, lens,
-                     c_log2, q_scale, k_scale, per_head, n_qt, (int)total);
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H, Tq_max, q_lens,
+                     Tk_max, k_lens, c_log2, q_scale, k_scale, per_head, n_qt, (int)total);
   return hipGetLastError();
 }
 

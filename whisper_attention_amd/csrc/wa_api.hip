@@ -177,7 +177,26 @@ wa_status wa_encoder_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, w
   if (!tile_rows_fit(ks.t, 2) || !tile_rows_fit(vs.t, 2)) return WA_ERR_UNSUPPORTED;
   wa_status st = check_device();
   if (st != WA_OK) return st;
-  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
+  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, T_max, lens,
+                                     causal, softmax_scale, nullptr, nullptr, 0, stream));
+}
+
+wa_status wa_cross_attn(const uint16_t *q, wa_strides qs, const uint16_t *k, wa_strides ks,
+                        const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B, int H,
+                        int T_q, int T_k, int head_dim, const int32_t *q_lens,
+                        const int32_t *k_lens, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o) return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || T_q <= 0 || T_k <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  if (!bf16_layout_ok(q, qs) || !bf16_layout_ok(k, ks) || !bf16_layout_ok(v, vs) ||
+      !bf16_layout_ok(o, os))
+    return WA_ERR_UNSUPPORTED;
+  if ((long)B * H * ((T_q + 127) / 128) > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  if (!tile_rows_fit(ks.t, 2) || !tile_rows_fit(vs.t, 2)) return WA_ERR_UNSUPPORTED;
+  wa_status st = check_device();
+  if (st != WA_OK) return st;
+  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_q, q_lens, T_k, k_lens, 0,
                                      softmax_scale, nullptr, nullptr, 0, stream));
 }
 
@@ -199,9 +218,9 @@ wa_status wa_encoder_attn_fp8qk(const uint8_t *q, wa_strides qs, const float *q_
   if (!tile_rows_fit(ks.t, 1) || !tile_rows_fit(vs.t, 2)) return WA_ERR_UNSUPPORTED;
   wa_status st = check_device();
   if (st != WA_OK) return st;
-  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, causal,
-                                     softmax_scale, q_scale, k_scale, gran == WA_SCALE_PER_HEAD,
-                                     stream));
+  return from_hip(wa::launch_encoder(q, qs, k, ks, v, vs, o, os, B, H, T_max, lens, T_max, lens,
+                                     causal, softmax_scale, q_scale, k_scale,
+                                     gran == WA_SCALE_PER_HEAD, stream));
 }
 
 size_t wa_decode_attn_workspace_size(int B, int H, int cache_len) {

@@ -62,10 +62,13 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
 
 // ---- encoder / prefill attention ----------------------------------------
 // q_scale == nullptr: bf16 Q and K.  Otherwise Q and K are E4M3 codes with
-// those dequantization scales ([1], or [H] when per_head).
+// those dequantization scales ([1], or [H] when per_head).  Queries
+// i < q_lens[b] of Tq_max attend keys j < k_lens[b] of Tk_max (a null
+// length array means the full size); causal needs the same sequence for both.
 hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_strides ks,
                           const uint16_t *v, wa_strides vs, uint16_t *o, wa_strides os, int B,
-                          int H, int T_max, const int32_t *lens, int causal, float softmax_scale,
+                          int H, int Tq_max, const int32_t *q_lens, int Tk_max,
+                          const int32_t *k_lens, int causal, float softmax_scale,
                           const float *q_scale, const float *k_scale, int per_head,
                           hipStream_t stream);
 

@@ -32,6 +32,7 @@ TID_SK_CODES, TID_SV_CODES = 8, 9          # self-attention cache codes
 TID_XK_SCALE, TID_XV_SCALE = 10, 11
 TID_SK_SCALE, TID_SV_SCALE = 12, 13
 TID_KV_K, TID_KV_V = 14, 15                # bf16 K/V to be quantized
+TID_XK_BF16, TID_XV_BF16 = 16, 17          # bf16 cross-attention K/V (encoder frames)
 
 
 def rng(seed, tid):
@@ -115,6 +116,10 @@ CONFIGS = {
                     gran="head"),
     # encoder at the shorter windows: 10-s (500 frames) and 15-s (750
     # frames) chunks, batches sized to the same B*T^2 work as enc_l3
+    # decoder prompt prefill attending to the 1500 encoder frames:
+    # prompt lengths U[4,224], bf16 K/V with 1% outliers x20
+    "prefill_cross": dict(B=128, H=20, T=224, lo=4, hi=224, T_k=ENC_FRAMES, outlier_p=0.01,
+                          outlier_mult=20.0),
     "enc_10s": dict(B=144, H=20, T=500),
     "enc_15s": dict(B=64, H=20, T=750),
     # long audio: 256 chunks (thirty per 15-minute file), Zipf(1.2) self
@@ -138,6 +143,15 @@ def prefill_inputs(B, H, T, lo, hi, outlier_p, outlier_mult, seed=0):
     k = bf16_normal(shape, seed, TID_K, outlier_p, outlier_mult)
     v = bf16_normal(shape, seed, TID_V, outlier_p, outlier_mult)
     return q, k, v, lens_uniform(B, lo, hi, seed)
+
+
+def cross_inputs(B, H, Tq, Tk, outlier_p=0.0, outlier_mult=20.0, seed=0):
+    """bf16 Q [B][Tq][H][64] (N(0,1)) and K, V [B][Tk][H][64] (N(0,1) with
+    outliers)."""
+    q = bf16_normal((B, Tq, H, HEAD_DIM), seed, TID_Q)
+    k = bf16_normal((B, Tk, H, HEAD_DIM), seed, TID_XK_BF16, outlier_p, outlier_mult)
+    v = bf16_normal((B, Tk, H, HEAD_DIM), seed, TID_XV_BF16, outlier_p, outlier_mult)
+    return q, k, v
 
 
 def decode_inputs(B, H, L, lens, gran, seed=0, which="self"):
