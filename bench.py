@@ -457,6 +457,17 @@ def encoder_fp8qk(steps, g_seed):
     return res
 
 
+def mfma_ceilings():
+    """What the matrix cores sustain on this GPU now: back-to-back dense
+    products (libwa_diag.so), bf16 and fp8, with the shader clock under that
+    load.  The published peaks assume 2.4 GHz."""
+    from whisper_attention_amd import diag
+    res = {d: diag.mfma_ceiling(d, iters=4096, reps=20) for d in ("bf16", "fp8")}
+    res["note"] = ("v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x64_f8f6f4 on four independent accumulators, "
+                   "2 blocks of 4 waves per CU; sclk from s_memtime over s_memrealtime")
+    return res
+
+
 def cpu_baseline(budget_s):
     """The CPU oracle on a bounded sample of the encoder workload: whole
     (b, h) pairs of B=16 x H=20 x T=1500 until ``budget_s`` seconds pass."""
@@ -532,6 +543,7 @@ def main():
     windows = encoder_windows(args.steps, g_seed=1)
     enc_fp8 = encoder_fp8qk(args.steps, g_seed=3)
     xpre = cross_prefill(args.steps, g_seed=4)
+    ceiling = mfma_ceilings()
     graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
     codecs = codec_rates(wl, args.steps)
     if args.copy_calib:
@@ -599,9 +611,11 @@ def main():
         "decode_step_graph": graph_step,
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "prefill_cross_attn": xpre,
+        "mfma_ceiling": ceiling,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false, false> (encoder)",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),
+                     "frac_of_measured_ceiling": round(enc_tflops / ceiling["bf16"]["TFLOP/s"], 4),
                      "traffic": traffic("encoder_attn.hip", "encoder"), "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": 4 * 2.0 * wl.enc["B"] * wl.enc["H"] * wl.enc["T"] * HEAD_DIM},
         "roofline_decode": {"bound": "hbm", "kernel": "decode_partial_kernel",

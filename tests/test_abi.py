@@ -9,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wa.h")
+DIAG_HEADER = os.path.join(ROOT, "include", "wa_diag.h")
 
 
 @pytest.fixture(scope="module")
@@ -17,8 +18,8 @@ def wa():
     return wa
 
 
-def _declared():
-    txt = open(HEADER).read()
+def _declared(header=HEADER):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(wa_[a-z0-9_]+)\s*\(", txt)))
 
@@ -297,3 +298,18 @@ def test_binding_refuses_host_tensors_and_bad_vectors(wa):
         wa._vec(torch.ones(3, dtype=torch.int64), torch.int32, 3, "lens")
     with pytest.raises(ValueError, match="scale"):
         wa._vec(torch.ones(2, dtype=torch.float32), torch.float32, 20, "scale")
+
+
+def test_diag_library_exports_and_validates():
+    """The measurement probes (libwa_diag.so, include/wa_diag.h) load, export
+    what the header declares, and refuse bad arguments before any launch."""
+    from whisper_attention_amd import diag
+    names = _declared(DIAG_HEADER)
+    assert set(diag.EXPORTED) == set(names)
+    for n in names:
+        assert hasattr(diag.lib, n), n
+    assert diag.lib.wa_diag_mfma_ceiling(0, 512, 16, None, None) == 1
+    assert diag.lib.wa_diag_mfma_ceiling(2, 512, 16, FAKE, None) == 1
+    assert diag.lib.wa_diag_mfma_ceiling(0, 0, 16, FAKE, None) == 1
+    assert diag.lib.wa_diag_mfma_ceiling(1, 512, (1 << 20) + 1, FAKE, None) == 1
+    assert diag.lib.wa_diag_wall_clock_khz(None) == 1

@@ -1,4 +1,5 @@
-"""Build libwa.so (the C-ABI HIP library) in-tree for gfx950.
+"""Build libwa.so (the C-ABI HIP library) and libwa_diag.so (the
+measurement probes of include/wa_diag.h) in-tree for gfx950.
 
 Run as ``python whisper_attention_amd/build.py`` (by path: importing the package
 would load the library before it is rebuilt); ``__graft_entry__.build()``
@@ -12,6 +13,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libwa.so")
+DIAG_LIB = os.path.join(PKG, "libwa_diag.so")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -32,9 +34,8 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False, extra=()):
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
+def _link(srcs, lib, verbose, extra):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -45,8 +46,13 @@ def build(verbose=False, extra=()):
         raise RuntimeError("hipcc failed:\n" + out)
     if out.strip() and verbose:
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=False, extra=()):
+    _link(sorted(glob.glob(os.path.join(PKG, "csrc", "diag", "*.hip"))), DIAG_LIB, verbose, extra)
+    return _link(sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))), LIB, verbose, extra)
 
 
 if __name__ == "__main__":
