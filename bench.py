@@ -46,8 +46,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # code_hash) of the kernel source they were taken on: a changed kernel
 # reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("24fa7ac9fb1bab47", {"encoder": 251.98e6, "prefill": 148.25e6,
-                                              "fp8qk_30s": 190.51e6}),
+    "encoder_attn.hip": ("4caaffa6747d500b", {"encoder": 251.98e6, "prefill": 148.26e6,
+                                              "fp8qk_30s": 190.46e6, "prefill_cross": 1055.53e6}),
     "decode_attn.hip": ("90acdc967b200294", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("63eef794f2b6b3a5", {"cross": 368.69e6}),
 }
@@ -410,9 +410,17 @@ def cross_prefill(steps, g_seed):
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
     tf = 4.0 * H * Tk * HEAD_DIM * float(lens_np.sum()) / (us * 1e-6) / 1e12
+    # K and V (every frame) read once, Q and O over the valid rows: the bytes
+    # outweigh the flops (110 flop per byte against the chip's 312), so HBM
+    # is this call's roofline
+    algo = 2.0 * HEAD_DIM * H * (2.0 * B * Tk + 2.0 * float(lens_np.sum()))
+    gbps = algo / (us * 1e-6) / 1e9
     res = {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
            "us": round(us, 2), "B": B, "H": H, "T_q": Tq, "T_k": Tk, "q_lens": f"U[{cfg['lo']},{cfg['hi']}]",
-           "mean_q_len": round(float(lens_np.mean()), 1)}
+           "mean_q_len": round(float(lens_np.mean()), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": algo,
+                        "traffic": traffic("encoder_attn.hip", "prefill_cross")}}
     del q, k, v, o
     return res
 
