@@ -150,8 +150,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
       const int j = blk + i * 16 + r;
       ok[i] = j < j1;
       const uint32_t off = (uint32_t)min(j, j1 - 1) * ts + qd * 16;  // past the end: last valid row
-      kk[i] = *reinterpret_cast<const uint4 *>(kb + off);
-      vv[i] = *reinterpret_cast<const uint4 *>(vb + off);
+      kk[i] = load_stream(kb + off);
+      vv[i] = load_stream(vb + off);
     }
     float s[4];
 #pragma unroll

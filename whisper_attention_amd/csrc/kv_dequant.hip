@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void kv_dequant_kernel(
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
     const int t = t0 + r + u * kRowsPerPass;
-    if (t < n) v[u] = *reinterpret_cast<const uint4 *>(cp + (long)t * cs.t);
+    if (t < n) v[u] = load_stream(cp + (long)t * cs.t);
   }
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {

@@ -11,6 +11,18 @@
 
 namespace wa {
 
+// A 16-byte load that is not kept in the last-level cache, for data read once
+// (the cache codes that decode attention and the dequantise read): the
+// last-level cache then keeps what the kernels before wrote instead of
+// evicting -- and writing back -- it during these reads.  (The quantize's
+// second read of its input stays cached: the prefill attention that follows
+// reads the same K and V.)
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  const u32x4_nt v = __builtin_nontemporal_load(static_cast<const u32x4_nt *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- kv quantize --------------------------------------------------------
 struct QuantPlan {
   int pieces_per_row;   // H * 8: one piece = 8 bf16 = 16 bytes
