@@ -76,3 +76,60 @@ def test_captured_decode_step_equals_eager(gpu, B, H):
             assert torch.equal(L["o_s"].view(torch.int16), o_s.view(torch.int16)), (replay, i, "self")
             assert torch.equal(L["o_x"].view(torch.int16), o_x.view(torch.int16)), (replay, i, "cross")
             assert torch.equal(L["kc"], kc) and torch.equal(L["vc"], vc), (replay, i, "cache")
+
+
+def test_captured_prompt_step_equals_eager(gpu):
+    """The prompt side captured in one graph: the K/V cache fill with dynamic
+    per-head scales (wa_kv_quant_fp8_kv: amax, scale and encode kernels), the
+    causal prefill attention and the prompt cross-attention against encoder
+    frames (wa_cross_attn), then the encoder attention.  Three replays, with
+    eager work between them, equal the eager pass bit for bit (outputs,
+    codes and scales)."""
+    import whisper_attention_amd as wa
+    B, H, T, Tk, L = 16, 20, 224, 1500, 256
+    announce(f"prompt step in a HIP graph: B={B} H={H} T={T} frames={Tk}")
+    lens = to_dev(workloads.lens_uniform(B, 4, T, 21))
+    q = to_dev(workloads.bf16_normal((B, T, H, 64), 21, 1))
+    k = to_dev(workloads.bf16_normal((B, T, H, 64), 21, 2, 0.01, 20.0))
+    v = to_dev(workloads.bf16_normal((B, T, H, 64), 21, 3, 0.01, 20.0))
+    qx, kx, vx = (to_dev(t) for t in workloads.cross_inputs(2, H, T, Tk, seed=22))
+    kx, vx = kx[:1].expand(B, Tk, H, 64), vx[:1].expand(B, Tk, H, 64)   # one chunk's frames for every prompt
+    qe, ke, ve = (to_dev(t) for t in workloads.encoder_inputs(1, H, Tk, seed=23))
+    kc = torch.zeros((B, H, L, 64), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(H, dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    ws = torch.empty(2 * wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head"), dtype=torch.uint8, device="cuda")
+    o_p, o_x = torch.empty_like(q), torch.empty_like(q)
+    o_e = torch.empty_like(qe)
+
+    def step():
+        wa.wa_kv_quant_fp8_kv(k, v, kc, vc, ks, vs, "head", lens=lens, workspace=ws)
+        wa.wa_encoder_attn(q, k, v, out=o_p, lens=lens, causal=True, softmax_scale=0.125)
+        wa.wa_cross_attn(q, kx, vx, out=o_x, q_lens=lens, softmax_scale=0.125)
+        wa.wa_encoder_attn(qe, ke, ve, out=o_e, softmax_scale=0.125)
+
+    outs = (o_p, o_x, o_e, kc, vc, ks, vs)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for replay in range(3):
+        for t in outs:                          # eager work between replays
+            t.zero_()
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            a = t.view(torch.uint8) if t.dtype != torch.uint8 else t
+            b = r.view(torch.uint8) if r.dtype != torch.uint8 else r
+            assert torch.equal(a, b), (replay, i)
