@@ -46,8 +46,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # code_hash) of the kernel source they were taken on: a changed kernel
 # reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("4caaffa6747d500b", {"encoder": 251.98e6, "prefill": 148.26e6,
-                                              "fp8qk_30s": 190.46e6, "prefill_cross": 1055.53e6}),
+    "encoder_attn.hip": ("12d285ac173e253e", {"encoder": 246.84e6, "prefill": 148.39e6,
+                                              "fp8qk_30s": 185.15e6, "prefill_cross": 1358.93e6}),
     "decode_attn.hip": ("c6eb9e4527d97166", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("3ee61d3727638963", {"cross": 368.68e6}),
 }

@@ -4,11 +4,14 @@
 // whisper-blaze 0.1.8 ("Direct Kernel API"), placed in the model as in
 // "Unlocking the power of OpenAI's Whisper", section 3.
 //
-// One block = 4 waves = 256 queries of one (b, h); each wave owns 64 queries
-// (two 32-query MFMA blocks, so every K and V fragment read from LDS feeds
-// two MFMAs) and walks the keys in tiles of 64.  Two blocks share a CU
-// (one wave of each on every SIMD), so one block's matrix work runs while the
-// other's vector work does.
+// One block = 4 waves = 128 queries of one (b, h); each wave owns one
+// 32-query MFMA column block and walks the keys in tiles of 64.  A wave takes
+// 122 VGPRs and a block 40 KB of LDS, so four blocks share a CU (one wave of
+// each on every SIMD): while one wave's matrix work runs, the others' vector
+// work and waits fill the SIMD.  (64 queries per wave, two column blocks per
+// K and V fragment read, needs 218 VGPRs and so allows two blocks per CU: 5 %
+// slower on the 30-s encoder, 8 % on the 10-s window and 17 % on the prompt
+// prefill.)
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form, so the
 // accumulator's lane index is the query:
@@ -24,17 +27,16 @@
 // Each interval (one per key tile t) runs the matrix work -- P(t-1).V(t-1)
 // and S(t) = K(t).Q^T -- and then the softmax of tile t on the vector ALU.
 // Eight waves in two groups that alternate those phases under a shared
-// barrier were measured slower than these two independent four-wave blocks
-// per CU, and interleaving a wave's own P(t-1).V(t-1) with its exponentials
-// needs more registers than two waves per SIMD leave.
+// barrier were measured slower than independent four-wave blocks per CU.
 //
 // K and V tiles are copied global -> LDS by the asynchronous 16-byte
-// global_load_lds instruction (no register staging) into four stages:
-// interval t reads K of tile t and V of tile t-1 and starts the copy of tile
-// t+2, so every copy has two intervals to land; completion is waited for
-// explicitly (vmcnt) before the barrier that publishes a tile.  The interval
-// loop is unrolled by four so every LDS read names its stage with a constant
-// offset.  Tiles are stored row-major with an XOR swizzle of their 16-byte
+// global_load_lds instruction (no register staging) into two rings, K tile j
+// in K slot j % 2 and V tile j in V slot j % 3 (16 + 24 KB): interval t reads
+// K of tile t and V of tile t-1 and starts the copy of tile t+1 into the
+// slots whose last reads were in interval t-1, so every copy has one
+// interval to land; completion is waited for explicitly (vmcnt) before the
+// barrier that publishes a tile.  The interval loop is unrolled by six so
+// every LDS read names its slot with a constant offset.  Tiles are stored row-major with an XOR swizzle of their 16-byte
 // chunks (applied by choosing which global chunk each lane fetches, since the
 // LDS destination of that instruction is fixed per lane).  The V^T operand is
 // read with gfx950's transposing LDS read ds_read_b64_tr_b16: within each 16
@@ -66,12 +68,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
-constexpr int kQW = 64;                   // queries per wave (two 32-query MFMA blocks)
+constexpr int kNQ = 1;                    // 32-query MFMA column blocks per wave
+constexpr int kQW = 32 * kNQ;             // queries per wave
 constexpr int kBM = kWaves * kQW;         // queries per block
 constexpr int kCopies = 2;                // 8-row copy instructions per wave per K/V tile
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
-constexpr int kStageBytes = 2 * kTileBytes;  // K then V (an fp8 K tile uses the first half of its slot)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;             // lazy-rescale threshold, log2 units
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -138,15 +140,17 @@ __device__ __forceinline__ uint32_t copy_offset_k8(wa_strides ks, int max_row, i
   return (uint32_t)(min(row, max_row) * ks.t + chunk * 16);
 }
 
-// The LDS ring: four stages of one K tile and one V tile each.
-__shared__ __attribute__((aligned(1024))) uint8_t g_lds[4][kStageBytes];
+// The LDS rings: two slots of one K tile and three of one V tile (an fp8 K
+// tile uses the first half of its slot).
+__shared__ __attribute__((aligned(1024))) uint8_t g_kring[2][kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_vring[3][kTileBytes];
 
 // One asynchronous 16-byte-per-lane copy global -> LDS: lane l's 16 bytes,
 // read from base + voff, land at LDS byte address lds + 16*l.  Written out
 // (rather than with the compiler's global_load_lds builtin) because the
-// compiler cannot tell the stages apart across the interval's branches and
-// would wait for every copy in flight -- including the one two tiles ahead --
-// before each LDS read.  The instruction has no result register; completion
+// compiler cannot tell the slots apart across the interval's branches and
+// would wait for every copy in flight -- including the next tile's -- before
+// each LDS read.  The instruction has no result register; completion
 // is tracked explicitly with s_waitcnt vmcnt before the barrier that
 // publishes a tile.
 __device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t voff, uint32_t lds) {
@@ -156,19 +160,23 @@ __device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t voff, u
                : "memory", "m0");
 }
 
-// LDS byte address of stage `stage`, as the instruction's M0 wants it.
-__device__ __forceinline__ uint32_t lds_addr(int stage) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_lds[0][0] +
-         stage * kStageBytes;
+// LDS byte addresses of a K or V slot, as the instruction's M0 wants them.
+__device__ __forceinline__ uint32_t k_addr(int slot) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_kring[0][0] +
+         slot * kTileBytes;
+}
+__device__ __forceinline__ uint32_t v_addr(int slot) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_vring[0][0] +
+         slot * kTileBytes;
 }
 
-// Issue the asynchronous copy of the K/V tile that starts at row k0 into a
-// stage.  Wave w fills K rows and V rows [16w, 16w+16) of the stage, 8 rows
-// per copy instruction.
+// Issue the asynchronous copy of the K/V tile that starts at row k0 into K
+// slot kslot and V slot vslot.  Wave w fills K rows and V rows [16w, 16w+16)
+// of the slots, 8 rows per copy instruction.
 // With fp8 K (kFp8) the K tile is 4 KB: one 16-row copy per wave, rows
 // [16w, 16w+16), from byte offsets k8 (the full-tile offset) of a uint8 K.
 template <bool kFp8>
-__device__ __forceinline__ void issue_tile(int stage, const void *kp, wa_strides ks,
+__device__ __forceinline__ void issue_tile(int kslot, int vslot, const void *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
                                            const CopyOffsets (&full)[kCopies], uint32_t k8, int lane,
                                            int w) {
@@ -177,24 +185,24 @@ __device__ __forceinline__ void issue_tile(int stage, const void *kp, wa_strides
     const int row0 = (w * kCopies + i) * 8;
     // only the last tile can run past kend
     const CopyOffsets c = k0 + kBN <= kend ? full[i] : copy_offsets(ks, vs, kend - 1 - k0, lane, row0);
-    const uint32_t dst = lds_addr(stage) + row0 * 128;
+    const uint32_t dst = k_addr(kslot) + row0 * 128;
     if (!kFp8) copy16_to_lds(static_cast<const uint16_t *>(kp) + (long)k0 * ks.t, c.k, dst);
-    copy16_to_lds(vp + (long)k0 * vs.t, c.v, dst + kTileBytes);
+    copy16_to_lds(vp + (long)k0 * vs.t, c.v, v_addr(vslot) + row0 * 128);
   }
   if (kFp8) {
     const int row0 = w * 16;
     const uint32_t off = k0 + kBN <= kend ? k8 : copy_offset_k8(ks, kend - 1 - k0, lane, row0);
-    copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, lds_addr(stage) + row0 * 64);
+    copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, k_addr(kslot) + row0 * 64);
   }
 }
 
 // Per-wave state of the online softmax.
 struct WaveState {
-  bf16x8 qreg[2][4];   // Q^T operands [q block][dim chunk]
-  f32x16 oacc[2][2];   // O^T accumulators [d block][q block]
-  f32x4 lacc[2];       // row sums of P per q block (16x16 MFMA layout, see row_sum_selector)
-  float m_run[2];      // running max per query, exp2 domain
-  bf16x8 sel;          // 0/1 selector A operand of the row-sum MFMA
+  bf16x8 qreg[kNQ][4];   // Q^T operands [q block][dim chunk]
+  f32x16 oacc[2][kNQ];   // O^T accumulators [d block][q block]
+  f32x4 lacc[kNQ];       // row sums of P per q block (16x16 MFMA layout, see row_sum_selector)
+  float m_run[kNQ];      // running max per query, exp2 domain
+  bf16x8 sel;           // 0/1 selector A operand of the row-sum MFMA
 };
 
 // Per-lane LDS byte offsets of the operand reads (the same in every tile).
@@ -232,7 +240,7 @@ __device__ __forceinline__ ReadOffsets read_offsets(int lane) {
 // kb*32 + (r/8)*16 + half*8 + r%8 of the tile.
 template <bool kFp8>
 __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
-                                       const ReadOffsets &ro, f32x16 (&s)[2][2]) {
+                                       const ReadOffsets &ro, f32x16 (&s)[2][kNQ]) {
   if (kFp8) {
     // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3): the whole head dim in one
     // instruction; lane l gives K row l%32 and Q column l%32, dims
@@ -243,7 +251,7 @@ __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
       const uint4 a1 = *reinterpret_cast<const uint4 *>(kl + ro.k8[1] + kb * 2048);
       const i32x8 ka = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < kNQ; ++qb) {
         const uint4 b0 = __builtin_bit_cast(uint4, st.qreg[qb][0]);
         const uint4 b1 = __builtin_bit_cast(uint4, st.qreg[qb][1]);
         const i32x8 qv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
@@ -259,7 +267,7 @@ __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
     for (int c = 0; c < 4; ++c)
       ka[c] = *reinterpret_cast<const bf16x8 *>(kl + ro.k[c] + kb * 4096);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kNQ; ++qb) {
       s[kb][qb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -269,10 +277,10 @@ __device__ __forceinline__ void scores(const WaveState &st, const uint8_t *kl,
 }
 
 // P = exp2(S*c - m) for one tile, as bf16 P^T operands.
-__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][2], const float (&m)[2],
-                                            float c_log2, bf16x8 (&pb)[2][4]) {
+__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][kNQ], const float (&m)[kNQ],
+                                            float c_log2, bf16x8 (&pb)[kNQ][4]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     const float mneg = -m[qb];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -296,12 +304,12 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][2], const float
 // sums carry exactly as well).  Returns whether it moved; alpha[qb] is then
 // the factor that takes O and l from the old frame to the new one.
 template <bool kCausal>
-__device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][2], int k0, int len,
-                                         int wq_lo, float c_log2, int lane, float (&alpha)[2]) {
+__device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][kNQ], int k0, int len,
+                                         int wq_lo, float c_log2, int lane, float (&alpha)[kNQ]) {
   const int half = lane >> 5, col = lane & 31;
   if (k0 + kBN > len || (kCausal && k0 + kBN - 1 > wq_lo)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kNQ; ++qb) {
       // the key's offset in the tile is a constant per (kb, r): compare it
       // with this lane's limit instead of forming every key index
       int lim = len - 1 - k0 - half * 8;
@@ -316,20 +324,21 @@ __device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][2], int k
         }
     }
   }
-  float mt[2];
+  float mt[kNQ];
+  bool moved = false;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
     mt[qb] = max_with_lane_xor32(mx) * c_log2;
+    moved = moved || mt[qb] > st.m_run[qb] + kLazy;
   }
-  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m_run[0] + kLazy || mt[1] > st.m_run[1] + kLazy) == 0)
-    return false;
+  if (__builtin_amdgcn_ballot_w64(moved) == 0) return false;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     const float m_new = fmaxf(st.m_run[qb], mt[qb]);
     alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);   // 0 on the first tile
     st.m_run[qb] = m_new;
@@ -339,9 +348,9 @@ __device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][2], int k
 
 // O and the row sums from the old frame to the new one (after a tile max
 // moved the running max).
-__device__ __forceinline__ void rescale(WaveState &st, const float (&alpha)[2], int lane) {
+__device__ __forceinline__ void rescale(WaveState &st, const float (&alpha)[kNQ], int lane) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     st.oacc[0][qb] *= alpha[qb];
     st.oacc[1][qb] *= alpha[qb];
     // row sums: lane n < 16 holds query n in element 0 and query n+16 in
@@ -371,9 +380,9 @@ __device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
 // O^T += V^T . P^T for one tile.  V^T operands: lane holds dim db*32 + col and
 // keys c*16 + half*8 .. +8, gathered by the transposing read.
 __device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
-                                              const ReadOffsets &ro, const bf16x8 (&pb)[2][4]) {
+                                              const ReadOffsets &ro, const bf16x8 (&pb)[kNQ][4]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < kNQ; ++qb)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       st.lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.sel, pb[qb][c], st.lacc[qb], 0, 0, 0);
@@ -387,7 +396,7 @@ __device__ __forceinline__ void accumulate_pv(WaveState &st, const uint8_t *vl,
       va[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < kNQ; ++qb)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         st.oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], pb[qb][c], st.oacc[db][qb], 0, 0, 0);
@@ -405,29 +414,25 @@ struct Ctx {
   float c_log2;
 };
 
-// Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+2 is
-// copied into `ahead` (the stage of tile t-2, whose last reads were in
-// interval t-1).  The block's waves pass one barrier per interval.
+// Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+1 is
+// copied into K slot `kahead` (that of tile t-1) and V slot `vahead` (that of
+// tile t-2), whose last reads were in interval t-1.  The block's waves pass
+// one barrier per interval.
 template <bool kFp8>
-__device__ __forceinline__ void open_interval(int ahead, int t, const Ctx &x) {
+__device__ __forceinline__ void open_interval(int kahead, int vahead, int t, const Ctx &x) {
   // Keep every instruction of the previous interval above the barrier.
   __builtin_amdgcn_sched_barrier(0);
-  // This wave's copies of tile t are complete -- only tile t+1's copies
-  // (2*kCopies, or kCopies + 1 with fp8 K) may still be in flight -- and so
-  // are its LDS reads of interval
-  // t-1 (the immediate holds vmcnt in bits 3:0 and lgkmcnt 0).  Then a bare
-  // barrier (a workgroup fence would wait for tile t+1's copies too):
-  // afterwards tile t is in LDS for everyone and the stage of tile t-2 is free.
-  if (t + 1 < x.nt)
-    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0 + (kFp8 ? kCopies + 1 : 2 * kCopies));
-  else
-    __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
+  // This wave's copies of tile t are complete (nothing else is in flight),
+  // and so are its LDS reads of interval t-1.  Then a bare barrier:
+  // afterwards tile t is in LDS for everyone, and the slots read in interval
+  // t-1 are free for tile t+1.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if (t + 2 < x.nt)
-    issue_tile<kFp8>(ahead, x.kp, x.ks, x.vp, x.vs, (t + 2) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
+  if (t + 1 < x.nt)
+    issue_tile<kFp8>(kahead, vahead, x.kp, x.ks, x.vp, x.vs, (t + 1) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
@@ -440,15 +445,15 @@ __device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
 // of tile t on the vector ALU (the other block on the CU fills the matrix
 // cores meanwhile).  P(t) is carried to the next interval in `pa`.
 template <bool kCausal, bool kFp8>
-__device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], const uint8_t *cur,
-                                         const uint8_t *prev, int ahead, int t, const Ctx &x) {
-  open_interval<kFp8>(ahead, t, x);
-  if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev + kTileBytes, x.ro, pa);
+__device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[kNQ][4], const uint8_t *cur,
+                                         const uint8_t *prev, int kahead, int vahead, int t, const Ctx &x) {
+  open_interval<kFp8>(kahead, vahead, t, x);
+  if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev, x.ro, pa);
   if (wave_needs<kCausal>(t, x)) {
-    f32x16 s[2][2];
+    f32x16 s[2][kNQ];
     scores<kFp8>(st, cur, x.ro, s);
     __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
-    float alpha[2];
+    float alpha[kNQ];
     if (tile_max<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, alpha))
       rescale(st, alpha, x.lane);
     // An exponential costs two to four times the issue time of an FMA; the
@@ -456,7 +461,7 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], cons
     // which then issue in their shadow instead of before them.
     softmax_exp(s, st.m_run, x.c_log2, pa);
 #pragma unroll
-    for (int g = 0; g < 64; ++g) {
+    for (int g = 0; g < 32 * kNQ; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
     }
@@ -466,7 +471,7 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[2][4], cons
 // Rows i < len_q of o for a sequence with no key: the empty sum is zero.
 __device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int h, int q0, int len_q) {
   const int i = q0 + (int)threadIdx.x;
-  if (i >= len_q) return;
+  if ((int)threadIdx.x >= kBM || i >= len_q) return;
   uint4 *op = reinterpret_cast<uint4 *>(o + (long)b * os.b + (long)i * os.t + (long)h * os.h);
 #pragma unroll
   for (int c = 0; c < 8; ++c) op[c] = uint4{0u, 0u, 0u, 0u};
@@ -477,7 +482,7 @@ __device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int
 // Queries i < q_lens[b] (of Tq_max rows) attend keys j < k_lens[b] (of Tk_max
 // rows); the causal form needs both to be the same sequence.
 template <bool kCausal, bool kFp8>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(
     const void *__restrict__ q, wa_strides qs, const void *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int Tq_max, const int32_t *__restrict__ q_lens, int Tk_max, const int32_t *__restrict__ k_lens,
@@ -522,20 +527,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopies + i) * 8);
   x.k8 = copy_offset_k8(ks, kBN - 1, lane, w * 16);
-  issue_tile<kFp8>(0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
-  if (x.nt > 1) issue_tile<kFp8>(1, x.kp, ks, x.vp, vs, kBN, x.kend, x.co, x.k8, lane, w);
+  issue_tile<kFp8>(0, 0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
   x.ro = read_offsets(lane);
   if (x.wq_lo >= len) {
     // Every query of this wave lies past the query length (short prompts in
-    // a 256-row tile): it does its share of the copies and passes the same
+    // a query tile): it does its share of the copies and passes the same
     // barriers as the other waves, and computes nothing.
-    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8>((t + 2) & 3, t, x);
+    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8>((t + 1) & 1, (t + 1) % 3, t, x);
     return;
   }
 
   WaveState st;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     const int my_q = x.wq_lo + qb * 32 + col;
     if (kFp8) {
       // 32 code bytes, dims 32*half .. +32, in qreg[qb][0..1]
@@ -561,24 +565,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   // Consume the Q loads here, once: otherwise the loop-header merge leaves
   // them "in flight" for the compiler, which then waits for every outstanding
   // copy (vmcnt(0)) before the first Q use of each unrolled iteration.
-  asm volatile("" ::"v"(st.qreg[0][0]), "v"(st.qreg[0][1]), "v"(st.qreg[0][2]), "v"(st.qreg[0][3]),
-               "v"(st.qreg[1][0]), "v"(st.qreg[1][1]), "v"(st.qreg[1][2]), "v"(st.qreg[1][3]));
+#pragma unroll
+  for (int qb = 0; qb < kNQ; ++qb)
+    asm volatile("" ::"v"(st.qreg[qb][0]), "v"(st.qreg[qb][1]), "v"(st.qreg[qb][2]), "v"(st.qreg[qb][3]));
 
-  // intervals t = 0 .. nt: tile t's K and tile t-1's V; the stage of tile j
-  // is j % 4.
-  bf16x8 pa[2][4];
-  for (int t = 0; t <= x.nt; t += 4) {
-    interval<kCausal, kFp8>(st, pa, g_lds[0], g_lds[3], 2, t, x);
+  // intervals t = 0 .. nt: tile t's K and tile t-1's V; K of tile j is in K
+  // slot j % 2, V of tile j in V slot j % 3
+  bf16x8 pa[kNQ][4];
+  for (int t = 0; t <= x.nt; t += 6) {
+    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[2], 1, 1, t, x);
     if (t + 1 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_lds[1], g_lds[0], 3, t + 1, x);
+    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[0], 0, 2, t + 1, x);
     if (t + 2 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_lds[2], g_lds[1], 0, t + 2, x);
+    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[1], 1, 0, t + 2, x);
     if (t + 3 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_lds[3], g_lds[2], 1, t + 3, x);
+    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[2], 0, 1, t + 3, x);
+    if (t + 4 > x.nt) break;
+    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[0], 1, 2, t + 4, x);
+    if (t + 5 > x.nt) break;
+    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[1], 0, 0, t + 5, x);
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kNQ; ++qb) {
     const int my_q = x.wq_lo + qb * 32 + col;
     // row sum of query col: element 0 (col < 16) or 1 (col >= 16) of lane col%16
     const float l0 = __shfl(st.lacc[qb][0], col & 15, 64);
