@@ -116,3 +116,19 @@ def test_cross_prefill_full_size_sampled(gpu):
     torch.cuda.synchronize()
     rows = [0, 1, int(np.argmax(q_lens)), int(np.argmin(q_lens)), 50, 77, 100, 127]
     _check(out, q, k, v, q_lens, [Tk] * B, "cross prefill", rows=rows)
+
+
+def test_cross_every_ring_position(gpu):
+    """Key lengths of 1 to 14 tiles, whole and ragged, against query lengths
+    that end at every 32-row wave of a 128-row tile."""
+    import whisper_attention_amd as wa
+    k_lens = np.array([64 * n + r for n in range(14) for r in (0, 17) if 64 * n + r > 0], np.int32)
+    B, H, Tk = len(k_lens), 2, int(k_lens.max())
+    q_lens = np.array([1 + (37 * i) % 160 for i in range(B)], np.int32)
+    Tq = int(q_lens.max())
+    announce(f"cross every ring position: B={B} Tq={Tq} Tk={Tk}")
+    q, k, v = workloads.cross_inputs(B, H, Tq, Tk, seed=32)
+    out = _nan_out(B, Tq, H)
+    wa.wa_cross_attn(to_dev(q), to_dev(k), to_dev(v), out=out, q_lens=to_dev(q_lens), k_lens=to_dev(k_lens))
+    torch.cuda.synchronize()
+    _check(out, q, k, v, q_lens, k_lens, "cross ring positions")

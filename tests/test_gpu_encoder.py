@@ -167,3 +167,18 @@ def test_late_large_scores(gpu, lam, causal):
     lens = [700, 690]
     got = _gpu(wa, q, k, v, lens, causal)
     _check(got, q, k, v, lens, causal, f"late large scores lam={lam} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_ring_position(gpu, causal):
+    """Key ranges of 1 to 14 tiles, whole and ragged, in one batch: the loop
+    over key tiles (two K slots, three V slots, unrolled by six) ends at
+    every position of its unrolled body, and the query tiles (128 rows)
+    end at every wave."""
+    import whisper_attention_amd as wa
+    lens = [64 * n + r for n in range(14) for r in (0, 17) if 64 * n + r > 0]
+    B, H, T = len(lens), 2, max(lens)
+    announce(f"every ring position, causal={causal}: B={B} T={T} lens={lens}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=31)
+    got = _gpu(wa, q, k, v, lens, causal)
+    _check(got, q, k, v, lens, causal, f"ring positions causal={causal}")

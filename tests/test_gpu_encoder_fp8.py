@@ -137,3 +137,18 @@ def test_codes_from_the_quantize_kernel_and_strided_views(gpu):
         assert np.array_equal(got_s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
         assert np.array_equal(got_c.cpu().numpy()[valid], want_c[valid])
     _check(out.float().cpu().numpy(), qc, qs, kc, ks, v, lens, False, "head", "fp8qk from quantize kernel")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_ring_position(gpu, causal):
+    """fp8 K tiles through every position of the unrolled tile loop (1 to 14
+    tiles, whole and ragged), per-head scales."""
+    import whisper_attention_amd as wa
+    lens = [64 * n + r for n in range(14) for r in (0, 17) if 64 * n + r > 0]
+    B, H, T = len(lens), 2, max(lens)
+    announce(f"fp8qk every ring position, causal={causal}: B={B} T={T}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=33)
+    qc, qs = _codes(q, lens, "head")
+    kc, ks = _codes(k, lens, "head")
+    got = _run(wa, qc, qs, kc, ks, v, lens, causal, "head")
+    _check(got, qc, qs, kc, ks, v, lens, causal, "head", f"fp8qk ring positions causal={causal}")
