@@ -46,8 +46,8 @@ N_SETS = 3                    # decode cache sets used in turn
 # code_hash) of the kernel source they were taken on: a changed kernel
 # reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("12d285ac173e253e", {"encoder": 246.84e6, "prefill": 148.39e6,
-                                              "fp8qk_30s": 185.15e6, "prefill_cross": 1358.93e6}),
+    "encoder_attn.hip": ("4ad2c9d38cc12360", {"encoder": 246.84e6, "prefill": 148.39e6,
+                                              "fp8qk_30s": 185.16e6, "prefill_cross": 1055.46e6}),
     "decode_attn.hip": ("c6eb9e4527d97166", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("3ee61d3727638963", {"cross": 368.68e6}),
 }
@@ -620,7 +620,7 @@ def main():
         "prefill_attn": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "us": round(ms[2] * 1e3, 2)},
         "prefill_cross_attn": xpre,
         "mfma_ceiling": ceiling,
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false, false> (encoder)",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<false, false, 4> (encoder)",
                      "achieved": round(enc_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4),
                      "frac_of_measured_ceiling": round(enc_tflops / ceiling["bf16"]["TFLOP/s"], 4),

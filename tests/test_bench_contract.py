@@ -35,9 +35,9 @@ def test_traffic_is_reported_only_for_the_source_it_was_measured_on(tmp_path):
     import bench
     for src, (h, rows) in bench.TRAFFIC.items():
         path = os.path.join(ROOT, "whisper_attention_amd", "csrc", src)
-        assert bench.code_hash(path) == h, f"{src}: counters were taken on another version of the kernel"
+        current = bench.code_hash(path) == h
         for launch, val in rows.items():
-            assert bench.traffic(src, launch) == val
+            assert bench.traffic(src, launch) == (val if current else None)
     # a comment-only edit keeps the hash; a code edit changes it
     src = open(os.path.join(ROOT, "whisper_attention_amd", "csrc", "kv_dequant.hip")).read()
     a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"

@@ -11,7 +11,10 @@
 // work and waits fill the SIMD.  (64 queries per wave, two column blocks per
 // K and V fragment read, needs 218 VGPRs and so allows two blocks per CU: 5 %
 // slower on the 30-s encoder, 8 % on the 10-s window and 17 % on the prompt
-// prefill.)
+// prefill.)  A non-causal query range of 129 to 256 rows (a prompt attending
+// to the encoder frames) takes one block of eight waves per (b, h) instead,
+// so that K and V are copied from memory once rather than by two blocks
+// that drift apart and miss in L2.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form, so the
 // accumulator's lane index is the query:
@@ -67,11 +70,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 4;
+// Waves per block: 4 (128 queries), or 8 (256 queries) for a short
+// non-causal query range, whose one block per (b, h) then reads K and V once.
+template <int kW> constexpr int kCopiesOf = 8 / kW;  // 8-row copies per wave per K/V tile
 constexpr int kNQ = 1;                    // 32-query MFMA column blocks per wave
 constexpr int kQW = 32 * kNQ;             // queries per wave
-constexpr int kBM = kWaves * kQW;         // queries per block
-constexpr int kCopies = 2;                // 8-row copy instructions per wave per K/V tile
+template <int kW> constexpr int kBMOf = kW * kQW;   // queries per block
+constexpr int kMaxCopies = 2;
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -175,21 +180,22 @@ __device__ __forceinline__ uint32_t v_addr(int slot) {
 // of the slots, 8 rows per copy instruction.
 // With fp8 K (kFp8) the K tile is 4 KB: one 16-row copy per wave, rows
 // [16w, 16w+16), from byte offsets k8 (the full-tile offset) of a uint8 K.
-template <bool kFp8>
+template <bool kFp8, int kW>
 __device__ __forceinline__ void issue_tile(int kslot, int vslot, const void *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
-                                           const CopyOffsets (&full)[kCopies], uint32_t k8, int lane,
+                                           const CopyOffsets (&full)[kMaxCopies], uint32_t k8, int lane,
                                            int w) {
+  constexpr int kC = kCopiesOf<kW>;
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
-    const int row0 = (w * kCopies + i) * 8;
+  for (int i = 0; i < kC; ++i) {
+    const int row0 = (w * kC + i) * 8;
     // only the last tile can run past kend
     const CopyOffsets c = k0 + kBN <= kend ? full[i] : copy_offsets(ks, vs, kend - 1 - k0, lane, row0);
     const uint32_t dst = k_addr(kslot) + row0 * 128;
     if (!kFp8) copy16_to_lds(static_cast<const uint16_t *>(kp) + (long)k0 * ks.t, c.k, dst);
     copy16_to_lds(vp + (long)k0 * vs.t, c.v, v_addr(vslot) + row0 * 128);
   }
-  if (kFp8) {
+  if (kFp8 && w < 4) {  // four 16-row copies fill a 4 KB fp8 K tile
     const int row0 = w * 16;
     const uint32_t off = k0 + kBN <= kend ? k8 : copy_offset_k8(ks, kend - 1 - k0, lane, row0);
     copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, k_addr(kslot) + row0 * 64);
@@ -407,7 +413,7 @@ struct Ctx {
   const void *kp;
   const uint16_t *vp;
   wa_strides ks, vs;
-  CopyOffsets co[kCopies];
+  CopyOffsets co[kMaxCopies];
   uint32_t k8;     // fp8 K: this lane's copy offset within a full tile
   ReadOffsets ro;
   int nt, kend, len, wq_lo, lane, w;
@@ -418,7 +424,7 @@ struct Ctx {
 // copied into K slot `kahead` (that of tile t-1) and V slot `vahead` (that of
 // tile t-2), whose last reads were in interval t-1.  The block's waves pass
 // one barrier per interval.
-template <bool kFp8>
+template <bool kFp8, int kW>
 __device__ __forceinline__ void open_interval(int kahead, int vahead, int t, const Ctx &x) {
   // Keep every instruction of the previous interval above the barrier.
   __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +438,7 @@ __device__ __forceinline__ void open_interval(int kahead, int vahead, int t, con
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   if (t + 1 < x.nt)
-    issue_tile<kFp8>(kahead, vahead, x.kp, x.ks, x.vp, x.vs, (t + 1) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
+    issue_tile<kFp8, kW>(kahead, vahead, x.kp, x.ks, x.vp, x.vs, (t + 1) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
@@ -444,10 +450,10 @@ __device__ __forceinline__ bool wave_needs(int j, const Ctx &x) {
 // Interval t: P(t-1).V(t-1) and S(t) on the matrix cores, then the softmax
 // of tile t on the vector ALU (the other block on the CU fills the matrix
 // cores meanwhile).  P(t) is carried to the next interval in `pa`.
-template <bool kCausal, bool kFp8>
+template <bool kCausal, bool kFp8, int kW>
 __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[kNQ][4], const uint8_t *cur,
                                          const uint8_t *prev, int kahead, int vahead, int t, const Ctx &x) {
-  open_interval<kFp8>(kahead, vahead, t, x);
+  open_interval<kFp8, kW>(kahead, vahead, t, x);
   if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev, x.ro, pa);
   if (wave_needs<kCausal>(t, x)) {
     f32x16 s[2][kNQ];
@@ -469,9 +475,10 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[kNQ][4], co
 }
 
 // Rows i < len_q of o for a sequence with no key: the empty sum is zero.
+template <int kW>
 __device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int h, int q0, int len_q) {
   const int i = q0 + (int)threadIdx.x;
-  if ((int)threadIdx.x >= kBM || i >= len_q) return;
+  if ((int)threadIdx.x >= kBMOf<kW> || i >= len_q) return;
   uint4 *op = reinterpret_cast<uint4 *>(o + (long)b * os.b + (long)i * os.t + (long)h * os.h);
 #pragma unroll
   for (int c = 0; c < 8; ++c) op[c] = uint4{0u, 0u, 0u, 0u};
@@ -481,8 +488,8 @@ __device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int
 // dequantization scales q_scale / k_scale ([1], or [H] when per_head).
 // Queries i < q_lens[b] (of Tq_max rows) attend keys j < k_lens[b] (of Tk_max
 // rows); the causal form needs both to be the same sequence.
-template <bool kCausal, bool kFp8>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(
+template <bool kCausal, bool kFp8, int kW>
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(
     const void *__restrict__ q, wa_strides qs, const void *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int Tq_max, const int32_t *__restrict__ q_lens, int Tk_max, const int32_t *__restrict__ k_lens,
@@ -499,11 +506,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   if (kCausal) qt = n_qt - 1 - qt;  // longest rows first
   const int b = bh / H, h = bh - b * H;
   const int len = min(max(q_lens ? q_lens[b] : Tq_max, 0), Tq_max);
+  constexpr int kBM = kBMOf<kW>;
   const int q0 = qt * kBM;
   if (q0 >= len) return;
   const int len_k = min(max(k_lens ? k_lens[b] : Tk_max, 0), Tk_max);
   if (len_k == 0) {
-    zero_rows(o, os, b, h, q0, len);
+    zero_rows<kW>(o, os, b, h, q0, len);
     return;
   }
 
@@ -525,15 +533,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // exp2-domain multiplier
   x.c_log2 = kFp8 ? c_log2 * q_scale[per_head ? h : 0] * k_scale[per_head ? h : 0] : c_log2;
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopies + i) * 8);
+  for (int i = 0; i < kCopiesOf<kW>; ++i)
+    x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopiesOf<kW> + i) * 8);
   x.k8 = copy_offset_k8(ks, kBN - 1, lane, w * 16);
-  issue_tile<kFp8>(0, 0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
+  issue_tile<kFp8, kW>(0, 0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
   x.ro = read_offsets(lane);
   if (x.wq_lo >= len) {
     // Every query of this wave lies past the query length (short prompts in
     // a query tile): it does its share of the copies and passes the same
     // barriers as the other waves, and computes nothing.
-    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8>((t + 1) & 1, (t + 1) % 3, t, x);
+    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8, kW>((t + 1) & 1, (t + 1) % 3, t, x);
     return;
   }
 
@@ -573,17 +582,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // slot j % 2, V of tile j in V slot j % 3
   bf16x8 pa[kNQ][4];
   for (int t = 0; t <= x.nt; t += 6) {
-    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[2], 1, 1, t, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[2], 1, 1, t, x);
     if (t + 1 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[0], 0, 2, t + 1, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[0], 0, 2, t + 1, x);
     if (t + 2 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[1], 1, 0, t + 2, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[1], 1, 0, t + 2, x);
     if (t + 3 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[2], 0, 1, t + 3, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[2], 0, 1, t + 3, x);
     if (t + 4 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_kring[0], g_vring[0], 1, 2, t + 4, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[0], 1, 2, t + 4, x);
     if (t + 5 > x.nt) break;
-    interval<kCausal, kFp8>(st, pa, g_kring[1], g_vring[1], 0, 0, t + 5, x);
+    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[1], 0, 0, t + 5, x);
   }
 
 #pragma unroll
@@ -619,12 +628,17 @@ hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_stride
                           const int32_t *k_lens, int causal, float softmax_scale,
                           const float *q_scale, const float *k_scale, int per_head, hipStream_t stream) {
   const float c_log2 = softmax_scale * kLog2e;
-  const int n_qt = (Tq_max + kBM - 1) / kBM;
+  // one 256-query block per (b, h) for a non-causal range of 129..256
+  // queries, so K and V are read once; otherwise 128-query blocks
+  const bool wide = !causal && Tq_max > kBMOf<4> && Tq_max <= kBMOf<8>;
+  const int bm = wide ? kBMOf<8> : kBMOf<4>;
+  const int n_qt = (Tq_max + bm - 1) / bm;
   const long total = (long)B * H * n_qt;
-  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(kWaves * 64);
+  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block((wide ? 8 : 4) * 64);
   const bool fp8 = q_scale != nullptr;
-  auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
-                       : (fp8 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
+  auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true, 4> : attn_fwd_kernel<true, false, 4>)
+                       : wide ? (fp8 ? attn_fwd_kernel<false, true, 8> : attn_fwd_kernel<false, false, 8>)
+                              : (fp8 ? attn_fwd_kernel<false, true, 4> : attn_fwd_kernel<false, false, 4>);
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H, Tq_max, q_lens,
                      Tk_max, k_lens, c_log2, q_scale, k_scale, per_head, n_qt, (int)total);
   return hipGetLastError();
