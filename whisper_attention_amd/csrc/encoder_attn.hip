@@ -176,10 +176,10 @@ __device__ __forceinline__ uint32_t v_addr(int slot) {
 }
 
 // Issue the asynchronous copy of the K/V tile that starts at row k0 into K
-// slot kslot and V slot vslot.  Wave w fills K rows and V rows [16w, 16w+16)
-// of the slots, 8 rows per copy instruction.
-// With fp8 K (kFp8) the K tile is 4 KB: one 16-row copy per wave, rows
-// [16w, 16w+16), from byte offsets k8 (the full-tile offset) of a uint8 K.
+// slot kslot and V slot vslot.  Wave w of kW fills K rows and V rows
+// [w*64/kW, (w+1)*64/kW) of the slots, 8 rows per copy instruction.
+// With fp8 K (kFp8) the K tile is 4 KB: waves 0..3 make one 16-row copy each,
+// rows [16w, 16w+16), from byte offsets k8 (the full-tile offset) of a uint8 K.
 template <bool kFp8, int kW>
 __device__ __forceinline__ void issue_tile(int kslot, int vslot, const void *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
