@@ -39,9 +39,10 @@
 // slots whose last reads were in interval t-1, so every copy has one
 // interval to land; completion is waited for explicitly (vmcnt) before the
 // barrier that publishes a tile.  The interval loop is unrolled by six so
-// every LDS read names its slot with a constant offset.  Tiles are stored row-major with an XOR swizzle of their 16-byte
-// chunks (applied by choosing which global chunk each lane fetches, since the
-// LDS destination of that instruction is fixed per lane).  The V^T operand is
+// every LDS read names its slot with a constant offset.  Tiles are stored
+// row-major with an XOR swizzle of their 16-byte chunks (applied by choosing
+// which global chunk each lane fetches, since the LDS destination of that
+// instruction is fixed per lane).  The V^T operand is
 // read with gfx950's transposing LDS read ds_read_b64_tr_b16: within each 16
 // lanes it returns 4 keys x 1 dim per lane from 4 rows x 16 dims.
 //
