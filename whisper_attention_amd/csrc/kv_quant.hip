@@ -128,13 +128,17 @@ __global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restric
   const int g = blockIdx.x;
   float *__restrict__ scale = qt.scale[blockIdx.z];
   const uint32_t *pg = partial + ((long)blockIdx.z * gridDim.x + g) * n_blocks;
+  // Every load of a pass is in flight at once: the partials were written on
+  // other XCDs, so each read is a full memory round trip (a group of the
+  // prompt prefill has 1792 partials: one pass of seven loads per thread).
   uint32_t m = 0;
-  int j = threadIdx.x;
-  for (; j + 768 < n_blocks; j += 1024) {
-    const uint32_t a = pg[j], b = pg[j + 256], c = pg[j + 512], d = pg[j + 768];
-    m = max(m, max(max(a, b), max(c, d)));
+  for (int j0 = threadIdx.x; j0 < n_blocks; j0 += 256 * 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u * 256 < n_blocks ? pg[j0 + u * 256] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max(m, v[u]);
   }
-  for (; j < n_blocks; j += 256) m = max(m, pg[j]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
