@@ -313,3 +313,24 @@ def test_diag_library_exports_and_validates():
     assert diag.lib.wa_diag_mfma_ceiling(0, 0, 16, FAKE, None) == 1
     assert diag.lib.wa_diag_mfma_ceiling(1, 512, (1 << 20) + 1, FAKE, None) == 1
     assert diag.lib.wa_diag_wall_clock_khz(None) == 1
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c11"), ("c++", "-std=c++17")])
+def test_headers_compile_as_plain_c_and_cpp(tmp_path, lang, std):
+    """include/wa.h and include/wa_diag.h are a C ABI: a C (and a C++) file
+    that includes both and takes the address of every declared function
+    compiles with warnings as errors, against the ROCm runtime header only."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    names = _declared() + _declared(DIAG_HEADER)
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "wa.h"\n#include "wa_diag.h"\nint main(void) {\n' +
+                   "".join(f"  (void)&{n};\n" for n in names) + "  return 0;\n}\n")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run([cc, std, "-fsyntax-only", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
