@@ -132,3 +132,42 @@ def test_cross_every_ring_position(gpu):
     wa.wa_cross_attn(to_dev(q), to_dev(k), to_dev(v), out=out, q_lens=to_dev(q_lens), k_lens=to_dev(k_lens))
     torch.cuda.synchronize()
     _check(out, q, k, v, q_lens, k_lens, "cross ring positions")
+
+
+def test_cross_over_a_dequantised_fp8_cache(gpu):
+    """The composition the header describes for an fp8 cross cache: the
+    encoder frames' K and V quantized into E4M3 caches (wa_kv_quant_fp8_kv,
+    per-head dynamic scales), expanded back to bf16 (wa_kv_dequant_fp8), then
+    the prompt's cross-attention over them (wa_cross_attn).  Codes, scales
+    and the bf16 expansion bit for bit against the oracle's quantize and
+    dequantise; the attention against the oracle's cross_attention over the
+    oracle's expansion."""
+    import whisper_attention_amd as wa
+    from oracle import quant
+    B, H, Tq, Tk = 4, 3, 40, 300
+    announce(f"cross over a dequantised fp8 cache: B={B} H={H} Tq={Tq} Tk={Tk}")
+    q, k, v = workloads.cross_inputs(B, H, Tq, Tk, 0.01, 20.0, seed=34)
+    q_lens = np.array([40, 1, 17, 33], np.int32)
+    full = np.full(B, Tk, np.int32)
+    kc = torch.zeros((B, H, Tk, 64), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(H, dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    wa.wa_kv_quant_fp8_kv(to_dev(k), to_dev(v), kc, vc, ks, vs, "head", lens=to_dev(full))
+    kd = torch.empty((B, Tk, H, 64), dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    wa.wa_kv_dequant_fp8(kc, ks, "head", "e4m3", out=kd, lens=to_dev(full))
+    wa.wa_kv_dequant_fp8(vc, vs, "head", "e4m3", out=vd, lens=to_dev(full))
+    out = _nan_out(B, Tq, H)
+    wa.wa_cross_attn(to_dev(q), kd, vd, out=out, q_lens=to_dev(q_lens))
+    torch.cuda.synchronize()
+    ref = {}
+    for name, x, c, s, d in (("K", k, kc, ks, kd), ("V", v, vc, vs, vd)):
+        cache = np.zeros((B, H, Tk, 64), dtype=np.uint8)
+        sc = quant.quantize_kv(x.float().numpy(), full, np.zeros(B, np.int64), cache, quant.PER_HEAD)
+        assert np.array_equal(c.cpu().numpy(), cache), f"{name} codes"
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), sc.view(np.uint32)), f"{name} scales"
+        bits = quant.unfill_cache(cache, full, sc, quant.PER_HEAD, Tk)
+        assert np.array_equal(d.cpu().view(torch.int16).numpy().view(np.uint16), bits), f"{name} expansion"
+        ref[name] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    _check(out, q, ref["K"], ref["V"], q_lens, full, "cross over dequantised fp8 cache")
