@@ -15,8 +15,13 @@ seeded inputs already resident in HBM, at the large-v3 shapes:
 algorithmic flops per call over the call's average duration, measured with
 HIP events on the launch stream); the decode throughput in GB/s (algorithmic
 bytes: every cached K/V byte read once plus q and o) sits beside it, each
-with its fraction of the MI355X peak.  ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the encoder workload.  Before the W warmup steps,
+with its fraction of the MI355X peak.  Beside the step: the long-audio
+decode (B=256, Zipf self lengths, per-head scales), the small workload,
+the shorter encoder windows, the fp8 encoder, the codec calls and a
+captured decode step, each with per-call median, p10 and p90.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the encoder
+workload, and ``cpu_baseline_per_config`` on samples of the decode,
+long-audio, quantize and small workloads.  Before the W warmup steps,
 untimed steps run for --settle-ms (100 ms) while the GPU's clocks rise from
 idle; the JSON line records how many (settle_steps).
 
@@ -70,6 +75,28 @@ def traffic(source, launch):
     if code_hash(os.path.join(ROOT, "whisper_attention_amd", "csrc", source)) != sha:
         return None
     return values[launch]
+
+
+def dist_us(ms):
+    """Per-call times (ms) -> mean, median, p10 and p90 in microseconds."""
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"mean": round(float(a.mean()), 2), "median": round(float(np.median(a)), 2),
+            "p10": round(float(np.percentile(a, 10)), 2), "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def time_calls(fn, steps, warm=3):
+    """Per-call event times (ms) of ``fn(i)`` for i in range(steps), events
+    on torch's current stream, the stream every wa_* call launches on."""
+    for i in range(warm):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
 
 
 def parse():
@@ -479,6 +506,114 @@ def mfma_ceilings():
     return res
 
 
+def fill_caches(wa, B, H, L, lens, gran, g):
+    """K and V E4M3 caches [B][H][L][64] with dynamic scales, filled by the
+    quantize kernel from N(0,1) bf16 (untimed)."""
+    out = []
+    for _ in range(2):
+        src = gen_bf16((B, L, H, HEAD_DIM), g)
+        c = torch.zeros((B, H, L, HEAD_DIM), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(H if gran == "head" else 1, dtype=torch.float32, device="cuda")
+        wa.wa_kv_quant_fp8(src, c, sc, gran, lens=lens)
+        del src
+        out.append((c, sc))
+    return out
+
+
+def decode_long(steps, g_seed):
+    """The long-audio decode step: B=256 sequences (thirty 30-s chunks per
+    15-minute file, from 8-9 files), 20 heads; cross-attention over 1500 E4M3
+    frames of each sequence's own chunk, then self-attention over a cache of
+    length min(Zipf(1.2), 448); per-head scales (each computed over the whole
+    batch by one quantize call).  N_SETS independent cache sets in turn
+    (3.8 GB, beyond the 256 MB last-level cache)."""
+    import workloads
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["long"]
+    B, H, Lx, cap = cfg["B"], cfg["H"], cfg["cross_len"], cfg["cap"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    lens_h = workloads.lens_zipf(B, cfg["zipf_a"], cap, 0)
+    lens_s = torch.from_numpy(lens_h).cuda()
+    lens_x = torch.full((B,), Lx, dtype=torch.int32, device="cuda")
+    sets = [(fill_caches(wa, B, H, Lx, None, "head", g), fill_caches(wa, B, H, cap, lens_s, "head", g))
+            for _ in range(N_SETS)]
+    q = gen_bf16((B, H, HEAD_DIM), g)
+    o_x, o_s = torch.empty_like(q), torch.empty_like(q)
+    ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, cap)), dtype=torch.uint8, device="cuda")
+
+    def cross(i):
+        (kc, ks), (vc, vs) = sets[i % N_SETS][0]
+        wa.wa_decode_attn(q, kc, vc, ks, vs, lens_x, "head", 0.125, out=o_x, workspace=ws_x)
+
+    def self_(i):
+        (kc, ks), (vc, vs) = sets[i % N_SETS][1]
+        wa.wa_decode_attn(q, kc, vc, ks, vs, lens_s, "head", 0.125, out=o_s, workspace=ws_s)
+
+    def both(i):
+        cross(i)
+        self_(i)
+
+    qo = 2 * 2.0 * B * H * HEAD_DIM
+    bx = 2.0 * B * H * Lx * HEAD_DIM + qo
+    bs = 2.0 * float(lens_h.sum()) * H * HEAD_DIM + qo
+    t_step = time_calls(both, steps)
+    t_x = time_calls(cross, steps)
+    t_s = time_calls(self_, steps)
+    gb = (bx + bs) / (np.mean(t_step) * 1e-3) / 1e9
+    res = {"value": round(gb, 1), "unit": "GB/s", "frac": round(gb / PEAK_HBM_GBPS, 4),
+           "us": dist_us(t_step), "algorithmic_bytes": bx + bs,
+           "cross": {"GB/s": round(bx / (np.mean(t_x) * 1e-3) / 1e9, 1), "us": dist_us(t_x), "bytes": bx},
+           "self": {"GB/s": round(bs / (np.mean(t_s) * 1e-3) / 1e9, 1), "us": dist_us(t_s), "bytes": bs,
+                    "mean_len": round(float(lens_h.mean()), 1),
+                    "at_cap": round(float((lens_h == cap).mean()), 3)},
+           "config": f"B={B} H={H} cross {Lx} + self min(Zipf({cfg['zipf_a']}), {cap}), per-head E4M3 scales",
+           "context": f"cross then self per step, back to back, {N_SETS} cache sets in turn"}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def tiny(steps, g_seed):
+    """The small workload: B=1 chunk, 6 heads.  Encoder attention at T=1500;
+    a decode step against 1500 cross frames and a 64-token self cache
+    (per-tensor E4M3 scales), and the fill of those caches (dynamic per-tensor
+    scale).  Latency-bound: it fills few of the 256 compute units."""
+    import workloads
+    import whisper_attention_amd as wa
+    cfg = workloads.CONFIGS["tiny"]
+    B, H, T, Ls = cfg["B"], cfg["H"], cfg["T"], cfg["self_len"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(g_seed)
+    qe, ke, ve = (gen_bf16((B, T, H, HEAD_DIM), g) for _ in range(3))
+    oe = torch.empty_like(qe)
+    xk_src = gen_bf16((B, T, H, HEAD_DIM), g)
+    xkc = torch.zeros((B, H, T, HEAD_DIM), dtype=torch.uint8, device="cuda")
+    xks = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws_q = torch.empty(max(16, wa.wa_kv_quant_fp8_workspace_size(B, H, T, "tensor")), dtype=torch.uint8,
+                       device="cuda")
+    (xk, xs_k), (xv, xs_v) = fill_caches(wa, B, H, T, None, "tensor", g)
+    (sk, ss_k), (sv, ss_v) = fill_caches(wa, B, H, Ls, None, "tensor", g)
+    q = gen_bf16((B, H, HEAD_DIM), g)
+    o = torch.empty_like(q)
+    lx = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    ls = torch.full((B,), Ls, dtype=torch.int32, device="cuda")
+    ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, T)), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8, device="cuda")
+    legs = {
+        "encoder": lambda i: wa.wa_encoder_attn(qe, ke, ve, out=oe, softmax_scale=0.125),
+        "kv_quant_cross_k": lambda i: wa.wa_kv_quant_fp8(xk_src, xkc, xks, "tensor", workspace=ws_q),
+        "decode_cross": lambda i: wa.wa_decode_attn(q, xk, xv, xs_k, xs_v, lx, "tensor", 0.125, out=o,
+                                                    workspace=ws_x),
+        "decode_self": lambda i: wa.wa_decode_attn(q, sk, sv, ss_k, ss_v, ls, "tensor", 0.125, out=o,
+                                                   workspace=ws_s),
+    }
+    res = {name: dist_us(time_calls(fn, steps)) for name, fn in legs.items()}
+    res["config"] = f"B={B} H={H}: encoder T={T}; decode cross {T} + self {Ls}, per-tensor E4M3"
+    return res
+
+
 def cpu_baseline(budget_s):
     """The CPU oracle on a bounded sample of the encoder workload: whole
     (b, h) pairs of B=16 x H=20 x T=1500 until ``budget_s`` seconds pass."""
@@ -505,6 +640,84 @@ def cpu_baseline(budget_s):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} whole (b, h) pairs of the encoder workload (T=1500, D=64), float64 numpy, "
                       f"{el:.1f} s"}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _until(budget_s, unit):
+    """Run unit(i) until budget_s seconds have passed; -> (units done, seconds)."""
+    done, t0 = 0, time.perf_counter()
+    while True:
+        unit(done)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return done, el
+
+
+def cpu_baselines(budget_s):
+    """The oracle, as it stands, on bounded samples of the other workloads,
+    from seeded host inputs of the same shapes (float64 numpy attention over
+    explicitly dequantized caches; fp32 quantize): whole sequences until
+    ``budget_s`` seconds pass each, rated on the same algorithmic bytes or
+    flops as the GPU legs."""
+    import workloads
+    from oracle import attn, quant
+    res = {}
+    thr = _threads()
+    H = 20
+    # Dec-L3 / Long decode: one sequence (20 heads) per unit, cross then self
+    for name, lens_fn, gran in (("decode_dec_l3", lambda: workloads.lens_uniform(64, 1, 448, 0), "tensor"),
+                                ("decode_long", lambda: workloads.lens_zipf(256, 1.2, 448, 0), "head")):
+        lens = lens_fn()
+        g = quant.PER_TENSOR if gran == "tensor" else quant.PER_HEAD
+        q, xk, xv, xks, xvs, _ = workloads.decode_inputs(1, H, 1500, [1500], gran, 0, "cross")
+        _, sk, sv, sks, svs, _ = workloads.decode_inputs(1, H, 448, [448], gran, 0, "self")
+        qf, xk, xv, sk, sv = q.float().numpy(), xk.numpy(), xv.numpy(), sk.numpy(), sv.numpy()
+        nbytes = []
+
+        def unit(i, lens=lens, g=g, qf=qf, xk=xk, xv=xv, xks=xks, xvs=xvs, sk=sk, sv=sv, sks=sks, svs=svs,
+                 nbytes=nbytes):
+            n = int(lens[i % len(lens)])
+            attn.decode_attention(qf, xk, xv, xks, xvs, g, [1500], 0.125)
+            attn.decode_attention(qf, sk, sv, sks, svs, g, [n], 0.125)
+            nbytes.append(2.0 * H * 64 * (1500 + n) + 4 * 2.0 * H * 64)
+
+        done, el = _until(budget_s, unit)
+        res[name] = {"value": round(sum(nbytes) / el / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
+                     "sample": f"{done} sequences x {H} heads (cross 1500 + self of the workload's lengths in "
+                               f"turn), {el:.1f} s"}
+    # Prefill quantize: K of one prompt (per-head dynamic scales) per unit
+    lens = workloads.lens_uniform(128, 4, 224, 0)
+    x = workloads.bf16_normal((8, 224, H, 64), 0, workloads.TID_KV_K, 0.01, 20.0).float().numpy()
+    cache = np.zeros((1, H, 224, 64), np.uint8)
+    elems = []
+
+    def qunit(i):
+        n = int(lens[i % len(lens)])
+        quant.quantize_kv(x[i % 8:i % 8 + 1], [n], [0], cache, quant.PER_HEAD)
+        elems.append(n * H * 64)
+
+    done, el = _until(budget_s, qunit)
+    res["kv_quant_prefill"] = {"value": round(3.0 * sum(elems) / el / 1e9, 4), "unit": "GB/s", "cores": thr,
+                               "kind": "oracle",
+                               "sample": f"{done} prompts of the prefill lengths x {H} heads, one tensor, per-head "
+                                         f"dynamic scales, {el:.1f} s"}
+    # Tiny: the whole small workload once (encoder 6 heads at T=1500)
+    q, k, v = workloads.encoder_inputs(1, 6, 1500, seed=0)
+    t0 = time.perf_counter()
+    attn.dense_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), [1500], False, 0.125)
+    el = time.perf_counter() - t0
+    res["tiny_encoder"] = {"value": round(4.0 * 6 * 1500 ** 2 * 64 / el / 1e12, 5), "unit": "TFLOP/s",
+                           "us": round(el * 1e6, 1), "cores": thr, "kind": "oracle",
+                           "sample": "the whole small workload's encoder call (B=1, H=6, T=1500)"}
+    return res
 
 
 def main():
@@ -551,6 +764,10 @@ def main():
     torch.cuda.synchronize()
     dseg = np.array([[devs[i][j].elapsed_time(devs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     dms = dseg.mean(axis=0)
+    print("[bench] decode, long audio", file=sys.stderr, flush=True)
+    long_ = decode_long(args.steps, g_seed=5)
+    print("[bench] small workload", file=sys.stderr, flush=True)
+    tiny_ = tiny(args.steps, g_seed=6)
     windows = encoder_windows(args.steps, g_seed=1)
     enc_fp8 = encoder_fp8qk(args.steps, g_seed=3)
     xpre = cross_prefill(args.steps, g_seed=4)
@@ -567,6 +784,10 @@ def main():
 
     seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
     ms = seg.mean(axis=0)          # per-part average ms
+    dist = {name: dist_us(seg[:, j]) for j, name in enumerate(("encoder", "kv_quant", "prefill_attn",
+                                                                "decode_cross", "decode_self"))}
+    ddist = {name: dist_us(dseg[:, j]) for j, name in enumerate(("decode_cross", "decode_self",
+                                                                 "decode_self_append"))}
     ms_step = wall * 1e3 / args.steps
     enc_tflops = wl.enc_flops() / (ms[0] * 1e-3) / 1e12
     quant_gbps = wl.quant_bytes() / (ms[1] * 1e-3) / 1e9
@@ -617,6 +838,10 @@ def main():
                      "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
                      "note": "one wa_kv_quant_fp8_kv call (K and V): amax + scale + encode kernels"},
         **codecs,
+        "per_call_us": {"in_step": dist, "decode_alone": ddist,
+                        "note": "per-call event times over the timed steps: mean, median, p10, p90"},
+        "decode_long": long_,
+        "tiny": tiny_,
         "encoder_windows": windows,
         "encoder_fp8qk": enc_fp8,
         "decode_step_graph": graph_step,
@@ -641,6 +866,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        rec["cpu_baseline_per_config"] = cpu_baselines(args.cpu_seconds / 3)
     print(json.dumps(rec), flush=True)
 
 

@@ -1,18 +1,47 @@
-"""Shared helpers of the GPU parity tests (HIP library vs CPU oracle)."""
+"""Shared helpers of the GPU parity tests (HIP library vs CPU oracle).
+
+The attention parity bar, applied by :func:`assert_close`:
+
+1. The stated bar, max-abs 2e-2 and mean-abs 2e-3 of |got - want|, on every
+   output whose terms are at most 1 in size (M <= 1, where M = sum_j p_j |V_j|
+   / sum_j p_j is the weighted mean size of the values an output sums; the
+   oracle returns it).  With unit-variance data that is almost every output.
+2. On every output, whatever M: |got - want| <= 2^-7 * M + half an ulp of
+   bf16 at the output's magnitude.  This is the bf16 arithmetic of the path:
+   - the weights p_j are rounded to bf16 (relative 2^-9) and the row sum adds
+     the same rounded weights, so with p'_j = p_j (1 + d_j) the output moves
+     by sum_j p_j d_j (V_j - O) / sum_j p'_j, at most max|d| (M + |O|) /
+     (1 - max|d|) <= 2 max|d| M (1 + 2^-8);
+   - the fp32 scores (64 exact products summed in fp32, or the fp8 matrix
+     core's own summation) and the hardware exp2 add well under 2^-11 to
+     max|d| at these data sizes, so 2 max|d| stays under 2^-8 * 1.3, and
+     2^-7 leaves a factor 1.5 for it;
+   - the fp32 accumulation of P.V and the final 1/l multiply are ~2^-22
+     relative;
+   - the output is stored as bf16: half an ulp at |O|.
+   For M <= 1 this is tighter than item 1 (at most 0.0078 + half an ulp).
+   Where values of V reach 20-80 (the x20 outliers of the prompt workload),
+   item 2 is the one that binds: a bf16 output near 64 has half an ulp of
+   0.25 by itself, so no bf16 output above 8 in size can meet an absolute
+   2e-2.
+
+Without M (two GPU results compared with each other) only item 1 applies,
+on every output.
+"""
+import json
+import os
 import sys
 
 import numpy as np
 import torch
 
-# Tolerance for attention outputs against the oracle: max-abs 2e-2 and
-# mean-abs 2e-3 (the bf16-compute contract of the hot path), on the error
-# divided by max(1, M), where M = sum_j p_j |V_j| / sum_j p_j is the size of
-# the terms the output sums (the oracle returns it).  Rounding the weights or
-# the output to bf16 (relative 2^-9) moves an output by up to 2^-9 * M, so
-# with unit-variance V (M < 1) this is the plain absolute error, and with
-# x20 outliers in V (M up to ~80) the bound scales with the data.
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+REL_W = 2.0 ** -7           # weight-perturbation budget of item 2, times M
+
+# Where the parity figures are appended as JSON lines (one per comparison),
+# when set: the raw error table is built from it.
+LOG = os.environ.get("WA_PARITY_LOG")
 
 
 def announce(msg):
@@ -31,20 +60,51 @@ def to_dev(x, dtype=None):
     return t.to(dev())
 
 
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 numbers at |x| (8 significant bits): for
+    2^e <= |x| < 2^(e+1) that is 2^(e-8); the smallest normal binade below."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    _, e = np.frexp(a)                 # a = f * 2^e, 0.5 <= f < 1
+    return np.ldexp(1.0, e - 9)
+
+
 def assert_close(got, want, what, mag=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
     """got: tensor (any float dtype); want: float64 array of the same shape;
-    mag: the oracle's sum_j p_j |V_j| / sum_j p_j for each output (None: |want|)."""
+    mag: the oracle's M = sum_j p_j |V_j| / sum_j p_j per output, or None."""
     g = got.detach().float().cpu().numpy().astype(np.float64)
     w = np.asarray(want, dtype=np.float64)
-    m = np.abs(w) if mag is None else np.asarray(mag, dtype=np.float64)
-    assert g.shape == w.shape == m.shape, (what, g.shape, w.shape, m.shape)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     raw = np.abs(g - w)
-    err = raw / np.maximum(1.0, m)
-    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
-    raw_mx = float(raw.max()) if raw.size else 0.0
-    print(f"[parity] {what}: max_err={mx:.3e} mean_err={mean:.3e} (raw max-abs {raw_mx:.3e}, "
-          f"max M {float(m.max()) if m.size else 0.0:.3g}) n={err.size}", flush=True)
-    assert mx <= max_abs, f"{what}: max error {mx:.3e} > {max_abs}"
-    assert mean <= mean_abs, f"{what}: mean error {mean:.3e} > {mean_abs}"
-    return mx, mean
+    if mag is None:
+        small = np.ones(raw.shape, dtype=bool)
+        m = None
+    else:
+        m = np.asarray(mag, dtype=np.float64)
+        assert m.shape == w.shape, (what, m.shape, w.shape)
+        small = m <= 1.0
+    rs = raw[small]
+    mx_s = float(rs.max()) if rs.size else 0.0
+    mean_s = float(rs.mean()) if rs.size else 0.0
+    rec = {"what": what, "n": int(raw.size), "raw_max": float(raw.max()) if raw.size else 0.0,
+           "raw_mean": float(raw.mean()) if raw.size else 0.0, "n_m_le_1": int(rs.size),
+           "max_m_le_1": mx_s, "mean_m_le_1": mean_s}
+    ratio = None
+    if m is not None and raw.size:
+        bound = REL_W * m + half_ulp_bf16(np.maximum(np.abs(g), np.abs(w)))
+        ratio = raw / bound
+        i = int(np.argmax(ratio))
+        rec.update({"max_M": float(m.max()), "worst_ratio": float(ratio.flat[i]),
+                    "worst_err": float(raw.flat[i]), "worst_M": float(m.flat[i]),
+                    "worst_bound": float(bound.flat[i])})
+    print(f"[parity] {json.dumps(rec)}", flush=True)
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    assert mx_s <= max_abs, f"{what}: max-abs {mx_s:.3e} > {max_abs} on outputs with M <= 1"
+    assert mean_s <= mean_abs, f"{what}: mean-abs {mean_s:.3e} > {mean_abs} on outputs with M <= 1"
+    if ratio is not None:
+        assert rec["worst_ratio"] <= 1.0, (
+            f"{what}: error {rec['worst_err']:.3e} above 2^-7 M + half-ulp = {rec['worst_bound']:.3e} "
+            f"(M = {rec['worst_M']:.3g})")
+    return rec["raw_max"], rec["raw_mean"]

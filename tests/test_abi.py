@@ -334,3 +334,94 @@ def test_headers_compile_as_plain_c_and_cpp(tmp_path, lang, std):
                         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_binding_refuses_mismatched_shapes(wa):
+    """Every size a kernel uses comes from one tensor, so the binding checks
+    the others against it before any library call: a mismatch would be read
+    or written out of bounds on the device.  (CPU tensors: the shape check
+    comes first, so no pointer is ever taken.)"""
+    import torch
+    bf, u8, f32, i32 = torch.bfloat16, torch.uint8, torch.float32, torch.int32
+    q = torch.zeros((2, 8, 3, 64), dtype=bf)
+    short = torch.zeros((2, 7, 3, 64), dtype=bf)
+    for kw in ({"k": short}, {"v": short}, {"out": short}):
+        args = {"k": q, "v": q, "out": torch.empty_like(q)}
+        args.update(kw)
+        with pytest.raises(ValueError, match="expected shape"):
+            wa.wa_encoder_attn(q, args["k"], args["v"], out=args["out"])
+    with pytest.raises(ValueError, match="expected shape"):
+        wa.wa_cross_attn(q, torch.zeros((2, 5, 3, 64), dtype=bf), torch.zeros((2, 5, 3, 64), dtype=bf),
+                         out=short)
+    qc = torch.zeros((2, 8, 3, 64), dtype=u8)
+    s1 = torch.ones(1, dtype=f32)
+    with pytest.raises(ValueError, match="expected shape"):
+        wa.wa_encoder_attn_fp8qk(qc, s1, qc, s1, "tensor", q, out=short)
+    # decode: caches [B][H][L][64] and out [B][H][64] against q [B][H][64]
+    qd = torch.zeros((2, 3, 64), dtype=bf)
+    lens = torch.ones(2, dtype=i32)
+    ws = torch.zeros(16, dtype=u8)
+    good = torch.zeros((2, 3, 10, 64), dtype=u8)
+    for bad in (torch.zeros((1, 3, 10, 64), dtype=u8), torch.zeros((2, 4, 10, 64), dtype=u8),
+                torch.zeros((2, 3, 10, 32), dtype=u8)):
+        with pytest.raises(ValueError, match="expected shape"):
+            wa.wa_decode_attn(qd, bad, bad, s1, s1, lens, "tensor", workspace=ws)
+        with pytest.raises(ValueError, match="expected shape"):
+            wa.wa_decode_attn_append(qd, qd, qd, bad, bad, s1, s1, lens, "tensor", workspace=ws)
+    with pytest.raises(ValueError, match="expected shape"):
+        wa.wa_decode_attn(qd, good, good, s1, s1, lens, "tensor", out=torch.zeros((2, 2, 64), dtype=bf),
+                          workspace=ws)
+    with pytest.raises(ValueError, match="expected shape"):
+        wa.wa_decode_attn_append(qd, qd, qd, good, good, s1, s1, lens, "tensor",
+                                 out=torch.zeros((1, 3, 64), dtype=bf), workspace=ws)
+    # quantize: the cache [B][H][L][64] against x [B][T][H][64]
+    x = torch.zeros((2, 8, 3, 64), dtype=bf)
+    for bad in (torch.zeros((3, 3, 8, 64), dtype=u8), torch.zeros((2, 2, 8, 64), dtype=u8),
+                torch.zeros((2, 3, 8, 16), dtype=u8)):
+        with pytest.raises(ValueError, match="expected shape"):
+            wa.wa_kv_quant_fp8(x, bad, s1, "tensor", workspace=ws)
+        with pytest.raises(ValueError, match="expected shape"):
+            wa.wa_kv_quant_fp8_kv(x, x, bad, bad, s1, s1, "tensor", workspace=ws)
+
+
+def test_half_ulp_of_bf16_matches_the_format():
+    """The parity bar's output-rounding term: half the distance from a bf16
+    value to the next one up, checked against the bit patterns."""
+    import numpy as np
+    import torch
+    from tests.gpu_helpers import half_ulp_bf16
+    assert half_ulp_bf16(1.0) == 2.0 ** -8
+    assert half_ulp_bf16(1.99) == 2.0 ** -8
+    assert half_ulp_bf16(2.0) == 2.0 ** -7
+    assert half_ulp_bf16(-0.75) == 2.0 ** -9
+    assert half_ulp_bf16(64.0) == 0.25
+    bits = np.arange(0x0080, 0x7F7F, 7, dtype=np.int32)          # positive normal bf16 patterns
+    v = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    nxt = torch.from_numpy((bits + 1).astype(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(nxt - v, 2 * half_ulp_bf16(v))
+
+
+def test_parity_bar_rejects_errors_beyond_the_bf16_bound():
+    """assert_close applies the stated absolute bar where M <= 1 and the
+    derived 2^-7 M + half-ulp bound everywhere."""
+    import numpy as np
+    import torch
+    from tests.gpu_helpers import assert_close
+    want = np.array([0.5, -0.25, 40.0, 70.0])
+    mag = np.array([0.8, 0.9, 45.0, 70.0])
+    got = torch.tensor(want, dtype=torch.float64)
+    assert_close(got, want, "exact", mag=mag)
+    # within the bound at large M: 0.3 < 2^-7 * 45 + 0.125
+    assert_close(got + torch.tensor([0.0, 0.0, 0.3, 0.0], dtype=torch.float64), want, "large M", mag=mag)
+    with pytest.raises(AssertionError, match="2\\^-7 M"):
+        assert_close(got + torch.tensor([0.0, 0.0, 0.6, 0.0], dtype=torch.float64), want, "beyond", mag=mag)
+    # M <= 1: 0.009 on one of 100 outputs is inside the stated max-abs and
+    # mean-abs bars, but above 2^-7 * 0.8 + half-ulp
+    w100, m100 = np.full(100, 0.5), np.full(100, 0.8)
+    err = np.zeros(100)
+    err[7] = 0.009
+    with pytest.raises(AssertionError, match="2\\^-7 M"):
+        assert_close(torch.from_numpy(w100 + err), w100, "small", mag=m100)
+    # without M the stated bar applies to every output
+    with pytest.raises(AssertionError, match="max-abs"):
+        assert_close(got + torch.tensor([0.0, 0.0, 0.03, 0.0], dtype=torch.float64), want, "no M")

@@ -3,13 +3,17 @@ calls): per layer, the self-attention step with its append
 (wa_decode_attn_append) and the cross-attention (wa_decode_attn).  The
 calls allocate nothing, synchronise nothing and record no memset, so they
 capture; every replay must equal the eager step, with eager work and
-synchronisations between the replays."""
+synchronisations between the replays, and every replay is checked against
+the oracle: the appended codes bit for bit (a static-scale cache fill of
+the step's token at slot lens[b] - 1), both attention outputs within the
+parity bar."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from tests.gpu_helpers import announce, to_dev
+from oracle import attn, quant
+from tests.gpu_helpers import announce, assert_close, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +27,10 @@ def _layer_inputs(B, H, Ls, Lx, layers, seed):
         _, xk, xv, xks, xvs, _ = workloads.decode_inputs(B, H, Lx, np.full(B, Lx), "tensor", seed + layer,
                                                          "cross")
         lay.append(dict(
+            host=dict(kc=kc.numpy().copy(), vc=vc.numpy().copy(), ks=ks, vs=vs, lens_s=lens_s, xk=xk.numpy(),
+                      xv=xv.numpy(), xks=xks, xvs=xvs),
             q=to_dev(workloads.bf16_normal((B, H, 64), seed + layer, 95)),
+            qx=to_dev(workloads.bf16_normal((B, H, 64), seed + layer, 98)),
             kn=to_dev(workloads.bf16_normal((B, H, 64), seed + layer, 96)),
             vn=to_dev(workloads.bf16_normal((B, H, 64), seed + layer, 97)),
             kc=to_dev(kc), vc=to_dev(vc), ks=to_dev(ks), vs=to_dev(vs), lens_s=to_dev(lens_s),
@@ -38,10 +45,29 @@ def _step(wa, lay, ws_s, ws_x):
     for L in lay:
         wa.wa_decode_attn_append(L["q"], L["kn"], L["vn"], L["kc"], L["vc"], L["ks"], L["vs"], L["lens_s"],
                                  "head", 0.125, out=L["o_s"], workspace=ws_s)
-        # the layer's cross-attention query depends on the self-attention
-        # output in the model; here it reuses it as the query
-        wa.wa_decode_attn(L["o_s"], L["xk"], L["xv"], L["xks"], L["xvs"], L["lens_x"], "tensor", 0.125,
+        # the layer's cross-attention (its query has its own seeded input
+        # here, so that the oracle takes no input from the HIP path)
+        wa.wa_decode_attn(L["qx"], L["xk"], L["xv"], L["xks"], L["xvs"], L["lens_x"], "tensor", 0.125,
                           out=L["o_x"], workspace=ws_x)
+
+
+def _oracle(L):
+    """Expected caches and outputs of one layer's step, from the host inputs:
+    the step's token encoded with the stored per-head scales into slot
+    lens[b] - 1 of the self cache, then both attentions over the caches."""
+    h = L["host"]
+    kc, vc = h["kc"].copy(), h["vc"].copy()
+    n = np.asarray(h["lens_s"], np.int64)
+    ones = (n > 0).astype(np.int64)
+    dst = np.maximum(n - 1, 0)
+    quant.fill_cache(L["kn"].float().cpu().numpy()[:, None], ones, dst, kc, h["ks"], quant.PER_HEAD)
+    quant.fill_cache(L["vn"].float().cpu().numpy()[:, None], ones, dst, vc, h["vs"], quant.PER_HEAD)
+    o_s, m_s = attn.decode_attention(L["q"].float().cpu().numpy(), kc, vc, h["ks"], h["vs"], quant.PER_HEAD, n,
+                                     0.125, with_magnitude=True)
+    B = n.shape[0]
+    o_x, m_x = attn.decode_attention(L["qx"].float().cpu().numpy(), h["xk"], h["xv"], h["xks"], h["xvs"],
+                                     quant.PER_TENSOR, np.full(B, h["xk"].shape[2]), 0.125, with_magnitude=True)
+    return kc, vc, (o_s, m_s), (o_x, m_x)
 
 
 @pytest.mark.parametrize("B,H", [(64, 20), (1, 20)])
@@ -64,6 +90,7 @@ def test_captured_decode_step_equals_eager(gpu, B, H):
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
         _step(wa, lay, ws_s, ws_x)
+    want = [_oracle(L) for L in lay]
     for replay in range(3):
         for L in lay:                            # eager work between replays
             L["o_s"].fill_(float("nan"))
@@ -76,6 +103,11 @@ def test_captured_decode_step_equals_eager(gpu, B, H):
             assert torch.equal(L["o_s"].view(torch.int16), o_s.view(torch.int16)), (replay, i, "self")
             assert torch.equal(L["o_x"].view(torch.int16), o_x.view(torch.int16)), (replay, i, "cross")
             assert torch.equal(L["kc"], kc) and torch.equal(L["vc"], vc), (replay, i, "cache")
+            wkc, wvc, (ws_o, ws_m), (wx_o, wx_m) = want[i]
+            assert np.array_equal(L["kc"].cpu().numpy(), wkc), (replay, i, "K cache vs oracle")
+            assert np.array_equal(L["vc"].cpu().numpy(), wvc), (replay, i, "V cache vs oracle")
+            assert_close(L["o_s"], ws_o, f"graph replay {replay} layer {i} self B={B}", mag=ws_m)
+            assert_close(L["o_x"], wx_o, f"graph replay {replay} layer {i} cross B={B}", mag=wx_m)
 
 
 def test_captured_prompt_step_equals_eager(gpu):
@@ -84,7 +116,8 @@ def test_captured_prompt_step_equals_eager(gpu):
     causal prefill attention and the prompt cross-attention against encoder
     frames (wa_cross_attn), then the encoder attention.  Three replays, with
     eager work between them, equal the eager pass bit for bit (outputs,
-    codes and scales)."""
+    codes and scales) and the oracle: codes and scales bit for bit, the
+    attention outputs within the parity bar."""
     import whisper_attention_amd as wa
     B, H, T, Tk, L = 16, 20, 224, 1500, 256
     announce(f"prompt step in a HIP graph: B={B} H={H} T={T} frames={Tk}")
@@ -122,6 +155,20 @@ def test_captured_prompt_step_equals_eager(gpu):
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
         step()
+    # the oracle, from the host inputs
+    lh = lens.cpu().numpy()
+    qh, kh, vh = (t.float().cpu().numpy() for t in (q, k, v))
+    wkc = np.zeros((B, H, L, 64), np.uint8)
+    wvc = np.zeros_like(wkc)
+    zero = np.zeros(B, np.int64)
+    wks = quant.quantize_kv(kh, lh, zero, wkc, quant.PER_HEAD)
+    wvs = quant.quantize_kv(vh, lh, zero, wvc, quant.PER_HEAD)
+    w_p, m_p = attn.dense_attention(qh, kh, vh, lh, True, 0.125, with_magnitude=True)
+    w_x, m_x = attn.cross_attention(qh, kx.float().cpu().numpy(), vx.float().cpu().numpy(), lh,
+                                    np.full(B, Tk), 0.125, with_magnitude=True)
+    w_e, m_e = attn.dense_attention(qe.float().cpu().numpy(), ke.float().cpu().numpy(), ve.float().cpu().numpy(),
+                                    [Tk], False, 0.125, with_magnitude=True)
+    valid = np.arange(T)[None, :] < lh[:, None]
     for replay in range(3):
         for t in outs:                          # eager work between replays
             t.zero_()
@@ -133,3 +180,11 @@ def test_captured_prompt_step_equals_eager(gpu):
             a = t.view(torch.uint8) if t.dtype != torch.uint8 else t
             b = r.view(torch.uint8) if r.dtype != torch.uint8 else r
             assert torch.equal(a, b), (replay, i)
+        assert np.array_equal(kc.cpu().numpy(), wkc) and np.array_equal(vc.cpu().numpy(), wvc), replay
+        assert np.array_equal(ks.cpu().numpy().view(np.uint32), wks.view(np.uint32)), replay
+        assert np.array_equal(vs.cpu().numpy().view(np.uint32), wvs.view(np.uint32)), replay
+        gp, gx = o_p.float().cpu().numpy(), o_x.float().cpu().numpy()
+        assert_close(torch.from_numpy(gp[valid]), w_p[valid], f"graph replay {replay} prefill", mag=m_p[valid])
+        assert_close(torch.from_numpy(gx[valid]), w_x[valid], f"graph replay {replay} prompt cross",
+                     mag=m_x[valid])
+        assert_close(o_e, w_e, f"graph replay {replay} encoder", mag=m_e)

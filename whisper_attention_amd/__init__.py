@@ -168,6 +168,22 @@ def _bits(t, dtype):
     return t
 
 
+def _shape(t, want, what):
+    """Refuse a tensor whose shape differs from ``want`` (None entries are
+    free): the kernels take every size from one tensor, so a mismatched one
+    would be read or written out of its bounds."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = "][".join("*" if w is None else str(w) for w in want)
+        raise ValueError(f"{what}: expected shape [{shown}], got {list(got)}")
+
+
+def _same_device(ref, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"every tensor must be on {ref.device}; got one on {t.device}")
+
+
 def wa_kv_quant_fp8_workspace_size(B, H, T_max, gran):
     return int(lib.wa_kv_quant_fp8_workspace_size(B, H, T_max, _gran(gran)))
 
@@ -194,6 +210,8 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
     _bits(cache, torch.uint8)
     _bits(scale, torch.float32)
     B, T, H, D = x.shape
+    _shape(cache, (B, H, None, D), "cache")
+    _same_device(x, cache, scale, lens, dst_start, workspace)
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
@@ -222,6 +240,8 @@ def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3
     if k.shape != v.shape or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k/v and their caches must share shapes, and the caches their strides")
     B, T, H, D = k.shape
+    _shape(k_cache, (B, H, None, D), "k_cache")
+    _same_device(k, v, k_cache, v_cache, k_scale, v_scale, lens, dst_start, workspace)
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
@@ -251,6 +271,7 @@ def wa_kv_dequant_fp8(cache, scale, gran, fmt, out=None, T_max=None, lens=None, 
     _bits(out, torch.bfloat16)
     if out.dim() != 4 or (out.shape[0], out.shape[2], out.shape[3]) != (B, H, D):
         raise ValueError(f"out must be [B={B}][T][H={H}][{D}], got {tuple(out.shape)}")
+    _same_device(cache, scale, out, lens)
     T = out.shape[1]
     g = _gran(gran)
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
@@ -268,6 +289,10 @@ def wa_encoder_attn(q, k, v, out=None, lens=None, causal=False, softmax_scale=0.
     B, T, H, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _bits(out, torch.bfloat16)
+    for t, name in ((k, "k"), (v, "v"), (out, "out")):
+        _shape(t, (B, T, H, D), name)
+    _same_device(q, k, v, out, lens)
     _check(lib.wa_encoder_attn(_ptr(q), _act_strides(q), _ptr(k), _act_strides(k), _ptr(v),
                                _act_strides(v), _ptr(out), _act_strides(out), B, H, T, D,
                                _vec(lens, torch.int32, B, "lens"), int(bool(causal)), float(softmax_scale),
@@ -289,6 +314,9 @@ def wa_encoder_attn_fp8qk(q, q_scale, k, k_scale, gran, v, out=None, lens=None, 
         raise ValueError("q, k and v must share the [B][T][H][64] shape")
     if out is None:
         out = torch.empty_like(v)
+    _bits(out, torch.bfloat16)
+    _shape(out, (B, T, H, D), "out")
+    _same_device(v, q, k, q_scale, k_scale, out, lens)
     g = _gran(gran)
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_encoder_attn_fp8qk(_ptr(q), _act_strides(q), _vec(q_scale, torch.float32, ng, "q_scale"),
@@ -310,6 +338,9 @@ def wa_cross_attn(q, k, v, out=None, q_lens=None, k_lens=None, softmax_scale=0.1
         raise ValueError("k and v must be [B][Tk][H][64] with q's B, H and head size")
     if out is None:
         out = torch.empty_like(q)
+    _bits(out, torch.bfloat16)
+    _shape(out, (B, Tq, H, D), "out")
+    _same_device(q, k, v, out, q_lens, k_lens)
     _check(lib.wa_cross_attn(_ptr(q), _act_strides(q), _ptr(k), _act_strides(k), _ptr(v),
                              _act_strides(v), _ptr(out), _act_strides(out), B, H, Tq, Tk, D,
                              _vec(q_lens, torch.int32, B, "q_lens"), _vec(k_lens, torch.int32, B, "k_lens"),
@@ -326,12 +357,16 @@ def wa_decode_attn(q, k_cache, v_cache, k_scale, v_scale, lens, gran, softmax_sc
     if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must share shape and strides")
     B, H, D = q.shape
+    _shape(k_cache, (B, H, None, D), "k_cache")
     L = k_cache.shape[2]
     if out is None:
         out = torch.empty_like(q)
+    _bits(out, torch.bfloat16)
+    _shape(out, (B, H, D), "out")
     if workspace is None:
         n = wa_decode_attn_workspace_size(B, H, L)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q, k_cache, v_cache, k_scale, v_scale, lens, out, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     g = _gran(gran)
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
@@ -357,12 +392,16 @@ def wa_decode_attn_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, l
     if k_new.stride() != v_new.stride() or k_new.shape != q.shape or v_new.shape != q.shape:
         raise ValueError("k_new and v_new must have q's shape and share strides")
     B, H, D = q.shape
+    _shape(k_cache, (B, H, None, D), "k_cache")
     L = k_cache.shape[2]
     if out is None:
         out = torch.empty_like(q)
+    _bits(out, torch.bfloat16)
+    _shape(out, (B, H, D), "out")
     if workspace is None:
         n = wa_decode_attn_workspace_size(B, H, L)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, lens, out, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     g = _gran(gran)
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
