@@ -14,6 +14,8 @@
  *                    (decoder self-attention or cross-attention)
  *   wa_decode_attn_append  the same for decoder self-attention, with the
  *                    step's token written into the cache in the same launch
+ *   wa_decode_attn_noalloc  wa_decode_attn with no workspace, for callers
+ *                    that cannot allocate
  *
  * Sources for what is computed:
  *   - "Blazingly fast whisper transcriptions with Inference Endpoints" (HF
@@ -68,7 +70,8 @@ typedef enum {
   WA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum */
   WA_ERR_UNSUPPORTED = 2,        /* head_dim != 64, misalignment, not gfx950 */
   WA_ERR_WORKSPACE_TOO_SMALL = 3,
-  WA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+  WA_ERR_HIP = 4,                /* a HIP runtime call or launch failed */
+  WA_ERR_TOO_LARGE = 5           /* more scratch than wa_decode_attn_noalloc holds */
 } wa_status;
 
 typedef enum {
@@ -331,6 +334,31 @@ wa_status wa_decode_attn_append(const uint16_t *q, wa_strides qs, const uint16_t
                                 const int32_t *lens, int B, int H, int head_dim,
                                 float softmax_scale, uint16_t *o, wa_strides os, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * wa_decode_attn_noalloc -- wa_decode_attn for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It takes no workspace and allocates
+ * nothing; inputs, outputs and errors are those of wa_decode_attn (same
+ * kernels, bit-identical results).
+ *
+ * The split-key partials go to a static device array of
+ * WA_DECODE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends.  A call whose partials (the bytes
+ * wa_decode_attn_workspace_size reports) exceed it returns WA_ERR_TOO_LARGE
+ * and launches nothing; with the current planner no call needs more than
+ * about 452 KB.  Every call on a GPU shares that GPU's array: two calls in
+ * flight at once on one GPU (on two streams, or from two host threads) race
+ * and must not overlap.
+ */
+#define WA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)512 * 1024)
+
+wa_status wa_decode_attn_noalloc(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                                 const uint8_t *v_cache, wa_strides cs, int cache_len,
+                                 const float *k_scale, const float *v_scale, wa_scale_gran gran,
+                                 const int32_t *lens, int B, int H, int head_dim,
+                                 float softmax_scale, uint16_t *o, wa_strides os,
+                                 hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *wa_status_string(wa_status s);

@@ -425,3 +425,48 @@ def test_parity_bar_rejects_errors_beyond_the_bf16_bound():
     # without M the stated bar applies to every output
     with pytest.raises(AssertionError, match="max-abs"):
         assert_close(got + torch.tensor([0.0, 0.0, 0.03, 0.0], dtype=torch.float64), want, "no M")
+
+
+def _noalloc(wa, **kw):
+    cs = wa.Strides(20 * 1500 * 64, 64, 1500 * 64)
+    ts = wa.Strides(20 * 64, 0, 64)
+    a = dict(q=FAKE, qs=ts, kc=FAKE, vc=FAKE, cs=cs, L=1500, ks=FAKE, vs=FAKE, gran=0, lens=FAKE, B=1, H=6,
+             D=64, sc=0.125, o=FAKE, os=ts)
+    a.update(kw)
+    return wa.lib.wa_decode_attn_noalloc(a["q"], a["qs"], a["kc"], a["vc"], a["cs"], a["L"], a["ks"], a["vs"],
+                                         a["gran"], a["lens"], a["B"], a["H"], a["D"], a["sc"], a["o"], a["os"],
+                                         None)
+
+
+def test_decode_noalloc_validation(wa):
+    """The no-allocation decode entry point checks its arguments as
+    wa_decode_attn does, on the host, before any HIP call."""
+    for name in ("q", "kc", "vc", "ks", "vs", "lens", "o"):
+        assert _noalloc(wa, **{name: None}) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _noalloc(wa, B=0) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _noalloc(wa, gran=3) == wa.WA_ERR_INVALID_ARGUMENT
+    assert _noalloc(wa, D=128) == wa.WA_ERR_UNSUPPORTED
+    assert _noalloc(wa, o=MIS) == wa.WA_ERR_UNSUPPORTED
+    assert "scratch" in wa.wa_status_string(wa.WA_ERR_TOO_LARGE)
+
+
+def test_decode_noalloc_scratch_covers_every_plan(wa):
+    """The static scratch array holds the split-key partials of any call:
+    the planner splits only below 640 (b, h) pairs, into at most
+    ceil(1024 / (B*H)) chunks, so no shape reaches the WA_ERR_TOO_LARGE
+    refusal (the check stays for a future planner)."""
+    worst = 0
+    for bh in list(range(1, 700)) + [1000, 5120, 65536]:
+        for L in (1, 63, 64, 65, 255, 256, 257, 448, 1500, 4096, 65536, 1 << 20):
+            worst = max(worst, wa.wa_decode_attn_workspace_size(1, bh, L))
+    assert 0 < worst <= wa.WA_DECODE_NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "WA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)512 * 1024)" in hdr
+    assert wa.WA_DECODE_NOALLOC_SCRATCH_BYTES == 512 * 1024
+
+
+def test_decode_noalloc_without_device_reports_hip_error(wa):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: a valid call with fake pointers would launch")
+    assert _noalloc(wa) == wa.WA_ERR_HIP

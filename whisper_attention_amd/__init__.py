@@ -12,6 +12,7 @@ The functions keep the C names:
 * ``wa_cross_attn``    decoder cross-attention for several query tokens (query
   and key lengths differ)
 * ``wa_decode_attn``   one query token per sequence against an E4M3 cache
+  (``wa_decode_attn_noalloc``: no workspace, for callers that cannot allocate)
 
 The library must have been built (``python whisper_attention_amd/build.py``);
 importing fails loudly when it is missing -- there is no fallback.
@@ -29,6 +30,9 @@ WA_ERR_INVALID_ARGUMENT = 1
 WA_ERR_UNSUPPORTED = 2
 WA_ERR_WORKSPACE_TOO_SMALL = 3
 WA_ERR_HIP = 4
+WA_ERR_TOO_LARGE = 5
+
+WA_DECODE_NOALLOC_SCRATCH_BYTES = 512 * 1024
 
 WA_SCALE_PER_TENSOR = 0
 WA_SCALE_PER_HEAD = 1
@@ -75,6 +79,8 @@ def _load():
     lib.wa_decode_attn.restype = I
     lib.wa_decode_attn_append.argtypes = [P, S, P, P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P, Z, P]
     lib.wa_decode_attn_append.restype = I
+    lib.wa_decode_attn_noalloc.argtypes = [P, S, P, P, S, I, P, P, I, P, I, I, I, F, P, S, P]
+    lib.wa_decode_attn_noalloc.restype = I
     lib.wa_decode_attn_workspace_size.argtypes = [I, I, I]
     lib.wa_decode_attn_workspace_size.restype = Z
     lib.wa_status_string.argtypes = [I]
@@ -86,8 +92,8 @@ lib = _load()
 
 EXPORTED = ("wa_kv_quant_fp8", "wa_kv_quant_fp8_fmt", "wa_kv_quant_fp8_kv", "wa_kv_dequant_fp8",
             "wa_kv_quant_fp8_workspace_size", "wa_encoder_attn", "wa_encoder_attn_fp8qk",
-            "wa_cross_attn", "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_workspace_size",
-            "wa_status_string")
+            "wa_cross_attn", "wa_decode_attn", "wa_decode_attn_append", "wa_decode_attn_noalloc",
+            "wa_decode_attn_workspace_size", "wa_status_string")
 
 
 def wa_status_string(status):
@@ -412,4 +418,31 @@ def wa_decode_attn_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, l
                                      _vec(lens, torch.int32, B, "lens"), B, H, D, float(softmax_scale),
                                      _ptr(out), _tok_strides(out), _ptr(workspace), ws_bytes,
                                      _stream(q, stream)))
+    return out
+
+
+def wa_decode_attn_noalloc(q, k_cache, v_cache, k_scale, v_scale, lens, gran, out, softmax_scale=0.125,
+                           stream=None):
+    """``wa_decode_attn`` without a workspace: the library keeps the split-key
+    partials in a static device array (WA_DECODE_NOALLOC_SCRATCH_BYTES per
+    GPU), so neither the call nor this wrapper allocates; ``out`` [B][H][64]
+    bf16 is required.  Calls on one GPU must not overlap in time."""
+    _bits(q, torch.bfloat16)
+    _bits(k_cache, torch.uint8)
+    _bits(v_cache, torch.uint8)
+    _bits(out, torch.bfloat16)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    B, H, D = q.shape
+    _shape(k_cache, (B, H, None, D), "k_cache")
+    _shape(out, (B, H, D), "out")
+    _same_device(q, k_cache, v_cache, k_scale, v_scale, lens, out)
+    L = k_cache.shape[2]
+    g = _gran(gran)
+    ng = 1 if g == WA_SCALE_PER_TENSOR else H
+    _check(lib.wa_decode_attn_noalloc(_ptr(q), _tok_strides(q), _ptr(k_cache), _ptr(v_cache),
+                                      _cache_strides(k_cache), L, _vec(k_scale, torch.float32, ng, "k_scale"),
+                                      _vec(v_scale, torch.float32, ng, "v_scale"), g,
+                                      _vec(lens, torch.int32, B, "lens"), B, H, D, float(softmax_scale),
+                                      _ptr(out), _tok_strides(out), _stream(q, stream)))
     return out

@@ -23,7 +23,9 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_arch_once[kMaxDevices];
 int g_arch_ok[kMaxDevices];
 
-wa_status check_device() {
+}  // namespace
+
+wa_status wa::check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return WA_ERR_HIP;
   if (dev >= kMaxDevices) return WA_ERR_UNSUPPORTED;
@@ -38,6 +40,10 @@ wa_status check_device() {
   if (g_arch_ok[dev] < 0) return WA_ERR_HIP;
   return g_arch_ok[dev] ? WA_OK : WA_ERR_UNSUPPORTED;
 }
+
+namespace {
+
+using wa::check_device;
 
 wa_status from_hip(hipError_t e) { return e == hipSuccess ? WA_OK : WA_ERR_HIP; }
 
@@ -58,6 +64,7 @@ const char *wa_status_string(wa_status s) {
     case WA_ERR_UNSUPPORTED: return "WA_ERR_UNSUPPORTED: head_dim != 64, misaligned pointer/stride, or device is not gfx950";
     case WA_ERR_WORKSPACE_TOO_SMALL: return "WA_ERR_WORKSPACE_TOO_SMALL";
     case WA_ERR_HIP: return "WA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case WA_ERR_TOO_LARGE: return "WA_ERR_TOO_LARGE: the call needs more scratch than the no-allocation entry point's static buffer holds";
   }
   return "unknown wa_status";
 }
@@ -230,6 +237,37 @@ size_t wa_decode_attn_workspace_size(int B, int H, int cache_len) {
 
 }  // extern "C"
 
+namespace wa {
+
+wa_status decode_args(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                      const uint8_t *v_cache, wa_strides cs, int cache_len, const float *k_scale,
+                      const float *v_scale, wa_scale_gran gran, const int32_t *lens, int B, int H,
+                      int head_dim, float softmax_scale, const uint16_t *o, wa_strides os,
+                      const uint16_t *k_new, const uint16_t *v_new, wa_strides ns, DecodeArgs *out) {
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !lens || !o)
+    return WA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
+  const wa_strides qs2 = {qs.b, 0, qs.h}, os2 = {os.b, 0, os.h}, ns2 = {ns.b, 0, ns.h};
+  if (!bf16_layout_ok(q, qs2) || !bf16_layout_ok(o, os2) || !u8_layout_ok(k_cache, cs) ||
+      !u8_layout_ok(v_cache, cs))
+    return WA_ERR_UNSUPPORTED;
+  if (k_new && (!bf16_layout_ok(k_new, ns2) || !bf16_layout_ok(v_new, ns2))) return WA_ERR_UNSUPPORTED;
+  if ((long)cache_len * cs.t > 0x7fffffffL) return WA_ERR_UNSUPPORTED;
+  const DecodePlan plan = decode_plan(B, H, cache_len);
+  if ((long)B * H * plan.n_split > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
+  out->plan = plan;
+  out->qs = qs2;
+  out->os = os2;
+  out->ns = ns2;
+  out->need = decode_workspace_bytes(B, H, plan);
+  return WA_OK;
+}
+
+}  // namespace wa
+
 namespace {
 
 wa_status decode_common(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
@@ -239,32 +277,21 @@ wa_status decode_common(const uint16_t *q, wa_strides qs, const uint8_t *k_cache
                         uint16_t *o, wa_strides os, void *workspace, size_t workspace_bytes,
                         hipStream_t stream, const uint16_t *k_new, const uint16_t *v_new,
                         wa_strides ns) {
-  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !lens || !o)
-    return WA_ERR_INVALID_ARGUMENT;
-  if (B <= 0 || H <= 0 || cache_len <= 0) return WA_ERR_INVALID_ARGUMENT;
-  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return WA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale)) return WA_ERR_INVALID_ARGUMENT;
-  if (head_dim != 64) return WA_ERR_UNSUPPORTED;
-  wa_strides qs2 = {qs.b, 0, qs.h}, os2 = {os.b, 0, os.h}, ns2 = {ns.b, 0, ns.h};
-  if (!bf16_layout_ok(q, qs2) || !bf16_layout_ok(o, os2) || !u8_layout_ok(k_cache, cs) ||
-      !u8_layout_ok(v_cache, cs))
-    return WA_ERR_UNSUPPORTED;
-  if (k_new && (!bf16_layout_ok(k_new, ns2) || !bf16_layout_ok(v_new, ns2))) return WA_ERR_UNSUPPORTED;
-  if ((long)cache_len * cs.t > 0x7fffffffL) return WA_ERR_UNSUPPORTED;
-  const wa::DecodePlan plan = wa::decode_plan(B, H, cache_len);
-  if ((long)B * H * plan.n_split > 0x7fffff00L) return WA_ERR_UNSUPPORTED;
-  const size_t need = wa::decode_workspace_bytes(B, H, plan);
-  if (need > 0) {
+  wa::DecodeArgs a;
+  wa_status st = wa::decode_args(q, qs, k_cache, v_cache, cs, cache_len, k_scale, v_scale, gran, lens,
+                                 B, H, head_dim, softmax_scale, o, os, k_new, v_new, ns, &a);
+  if (st != WA_OK) return st;
+  if (a.need > 0) {
     if (!workspace) return WA_ERR_INVALID_ARGUMENT;
     if (!aligned16(workspace)) return WA_ERR_UNSUPPORTED;
-    if (workspace_bytes < need) return WA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < a.need) return WA_ERR_WORKSPACE_TOO_SMALL;
   }
-  wa_status st = check_device();
+  st = wa::check_device();
   if (st != WA_OK) return st;
-  return from_hip(wa::launch_decode(q, qs2, k_cache, v_cache, cs, cache_len, k_scale, v_scale,
-                                    gran == WA_SCALE_PER_HEAD, lens, B, H, softmax_scale, o, os2,
-                                    static_cast<float *>(workspace), plan, stream, k_new, v_new,
-                                    ns2));
+  return from_hip(wa::launch_decode(q, a.qs, k_cache, v_cache, cs, cache_len, k_scale, v_scale,
+                                    gran == WA_SCALE_PER_HEAD, lens, B, H, softmax_scale, o, a.os,
+                                    static_cast<float *>(workspace), a.plan, stream, k_new, v_new,
+                                    a.ns));
 }
 
 }  // namespace

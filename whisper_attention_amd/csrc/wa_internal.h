@@ -64,6 +64,23 @@ struct DecodePlan {
 DecodePlan decode_plan(int B, int H, int cache_len);
 size_t decode_workspace_bytes(int B, int H, const DecodePlan &p);
 
+// Host-side checks of a decode call (wa_api.hip), shared by every decode
+// entry point; nothing here touches the device.  On WA_OK, `out` holds the
+// plan, the token strides with t zeroed, and the partials' byte count.
+struct DecodeArgs {
+  DecodePlan plan;
+  wa_strides qs, os, ns;
+  size_t need;
+};
+wa_status decode_args(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
+                      const uint8_t *v_cache, wa_strides cs, int cache_len, const float *k_scale,
+                      const float *v_scale, wa_scale_gran gran, const int32_t *lens, int B, int H,
+                      int head_dim, float softmax_scale, const uint16_t *o, wa_strides os,
+                      const uint16_t *k_new, const uint16_t *v_new, wa_strides ns, DecodeArgs *out);
+
+// The first call on each device checks that it is a gfx950.
+wa_status check_device();
+
 hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, const uint8_t *vc,
                          wa_strides cs, int cache_len, const float *k_scale,
                          const float *v_scale, int per_head, const int32_t *lens, int B, int H,
