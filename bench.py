@@ -154,7 +154,7 @@ class Workload:
         self.ksp = torch.zeros(H, dtype=torch.float32, device=dev)
         self.vsp = torch.zeros(H, dtype=torch.float32, device=dev)
         # K and V partials: twice the one-tensor workspace
-        self.ws_q = torch.empty(max(16, 2 * wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head")),
+        self.ws_q = torch.zeros(max(16, 2 * wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head")),
                                 dtype=torch.uint8, device=dev)
         # 4. decode step: caches filled once (untimed) by the quantize kernel
         self.dec = dict(B=64, H=20, Lx=1500, Ls=448)
@@ -591,7 +591,7 @@ def tiny(steps, g_seed):
     xk_src = gen_bf16((B, T, H, HEAD_DIM), g)
     xkc = torch.zeros((B, H, T, HEAD_DIM), dtype=torch.uint8, device="cuda")
     xks = torch.zeros(1, dtype=torch.float32, device="cuda")
-    ws_q = torch.empty(max(16, wa.wa_kv_quant_fp8_workspace_size(B, H, T, "tensor")), dtype=torch.uint8,
+    ws_q = torch.zeros(max(16, wa.wa_kv_quant_fp8_workspace_size(B, H, T, "tensor")), dtype=torch.uint8,
                        device="cuda")
     (xk, xs_k), (xv, xs_v) = fill_caches(wa, B, H, T, None, "tensor", g)
     (sk, ss_k), (sv, ss_v) = fill_caches(wa, B, H, Ls, None, "tensor", g)

@@ -115,7 +115,12 @@ typedef struct {
  *            earlier); values beyond 448 * scale saturate.
  * workspace  device scratch of at least wa_kv_quant_fp8_workspace_size()
  *            bytes (only used when compute_scale = 1; may be NULL otherwise).
- *            Its contents need no initialisation.
+ *            Its first 256 bytes hold a counter through which the last of
+ *            the scale kernel's blocks finds itself; it must be zero before
+ *            the first call that uses the workspace (a zero-filled
+ *            allocation), and every call leaves it zero again, so a
+ *            workspace reused call after call needs no further clearing.
+ *            The rest needs no initialisation.
  */
 wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_max,
                           int head_dim, const int32_t *lens, const int32_t *dst_start,
@@ -155,7 +160,10 @@ wa_status wa_kv_quant_fp8_fmt(const uint16_t *x, wa_strides xs, int B, int H, in
  *   ks and vs may differ.
  *
  * workspace  device scratch of at least 2 * wa_kv_quant_fp8_workspace_size()
- *            bytes when compute_scale = 1.
+ *            bytes when compute_scale = 1: K's part, then V's part starting
+ *            wa_kv_quant_fp8_workspace_size() bytes in, each with its own
+ *            256-byte counter at its start (zero before first use, left zero
+ *            by every call, as for wa_kv_quant_fp8).
  * Errors: those of wa_kv_quant_fp8_fmt; a null v, v_cache or v_scale is
  *   WA_ERR_INVALID_ARGUMENT.
  */

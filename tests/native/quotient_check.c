@@ -12,6 +12,13 @@
  * that sign (a tie at that point rounds to the even code, zero), so the codes
  * agree.
  *
+ * With a dynamic scale s = amax / FMAX the kernels drop both clamps (no
+ * encoded |x| exceeds amax, so no step can overflow); that form is checked
+ * too, for every finite bf16 x with |x| <= amax.  Its quotient may then lie
+ * a rounding above FMAX, where the format's largest code still applies: it
+ * must stay below FMAX (1 + 2^-10), far under the midpoint to the next
+ * binade.
+ *
  * usage: quotient_check STRIDE [e5m2]
  *          every STRIDE-th dynamic scale amax/FMAX over the positive finite
  *          bf16 amax, plus fixed edge scales; exit status 1 on a mismatch
@@ -38,6 +45,30 @@ static float method(float x, float s, float r) {
   return copysignf(q, x);
 }
 
+static float method_dyn(float x, float s, float r) {
+  const float a = fabsf(x);
+  const float q0 = a * r;
+  const float e = fmaf(-q0, s, a);
+  return copysignf(fmaf(e, r, q0), x);
+}
+
+static long check_dyn(float s, float amax) {
+  const float r = 1.0f / s;
+  long bad = 0;
+  for (uint32_t b = 0; b < 65536; ++b) {
+    const float x = from_bits(b << 16);
+    if (!isfinite(x) || fabsf(x) > amax) continue;
+    const float w = ieee(x, s), g = method_dyn(x, s, r);
+    if (to_bits(w) == to_bits(g)) continue;
+    if (fabsf(w) <= ZERO_BELOW && fabsf(g) <= ZERO_BELOW && signbit(w) == signbit(g)) continue;
+    if (fabsf(w) == FMAX && fabsf(g) > FMAX && fabsf(g) <= FMAX * (1.0f + 0x1p-10f) && signbit(w) == signbit(g))
+      continue;
+    if (bad < 3) printf("mismatch (dynamic): s=%a x=%a ieee=%a method=%a\n", s, x, w, g);
+    ++bad;
+  }
+  return bad;
+}
+
 static long check(float s) {
   const float r = 1.0f / s;
   long bad = 0;
@@ -61,9 +92,10 @@ int main(int argc, char **argv) {
   }
   long bad = 0, n = 0;
   for (uint32_t b = 1; b < 0x7f80; b += (uint32_t)stride) {   /* dynamic scales */
-    const float s = from_bits(b << 16) / FMAX;
+    const float amax = from_bits(b << 16), s = amax / FMAX;
     if (!(s >= 0x1p-80f && s <= 0x1p80f)) continue;
     bad += check(s);
+    bad += check_dyn(s, amax);
     ++n;
   }
   const float edge[] = {0x1p-80f, 0x1p80f, 0x1.fffffep79f, 0x1.000002p-80f, 1.0f, 0.125f,

@@ -132,7 +132,8 @@ def test_captured_prompt_step_equals_eager(gpu):
     vc = torch.zeros_like(kc)
     ks = torch.zeros(H, dtype=torch.float32, device="cuda")
     vs = torch.zeros_like(ks)
-    ws = torch.empty(2 * wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head"), dtype=torch.uint8, device="cuda")
+    half = wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head")
+    ws = torch.zeros(2 * half, dtype=torch.uint8, device="cuda")
     o_p, o_x = torch.empty_like(q), torch.empty_like(q)
     o_e = torch.empty_like(qe)
 
@@ -172,10 +173,14 @@ def test_captured_prompt_step_equals_eager(gpu):
     for replay in range(3):
         for t in outs:                          # eager work between replays
             t.zero_()
-        ws.fill_(0xA5)
+        # the partials need no initialisation; the counters at the start of
+        # each tensor's half are zero, as every call leaves them
+        for part in (ws[256:half], ws[half + 256:]):
+            part.fill_(0xA5)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        assert not ws[:256].any() and not ws[half:half + 256].any(), (replay, "counters not left at zero")
         for i, (t, r) in enumerate(zip(outs, ref)):
             a = t.view(torch.uint8) if t.dtype != torch.uint8 else t
             b = r.view(torch.uint8) if r.dtype != torch.uint8 else r

@@ -5,7 +5,8 @@ FMA correction (Markstein's method) for scales in [2^-80, 2^80].  This test
 compiles a C restatement of that sequence (tests/native/quotient_check.c)
 and compares it with IEEE division for every finite bf16 x, at every 16th
 dynamic scale amax/FMAX and at edge scales, for E4M3 (FMAX 448) and E5M2
-(FMAX 57344): the codes must agree everywhere.
+(FMAX 57344): the codes must agree everywhere.  The clamp-free form used
+with dynamic scales is checked over every |x| <= amax of each scale.
 The GPU tests then check the kernel itself against the oracle, bit for bit.
 """
 import os

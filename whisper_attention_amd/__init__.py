@@ -204,6 +204,8 @@ def wa_kv_quant_fp8(x, cache, scale, gran, lens=None, dst_start=None, compute_sc
 
     ``scale`` (float32, [1] or [H]) is written when ``compute_scale`` and read
     otherwise.  ``lens``/``dst_start`` are int32 device tensors [B] or None.
+    A ``workspace`` passed in must have been zero-filled before its first use
+    (every call leaves its counter at zero).
     """
     return wa_kv_quant_fp8_fmt(x, cache, scale, gran, "e4m3", lens, dst_start, compute_scale,
                                workspace, stream)
@@ -221,7 +223,8 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+        # zero-filled: the workspace begins with the scale kernel's counter
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_kv_quant_fp8_fmt(_ptr(x), _act_strides(x), B, H, T, D, _vec(lens, torch.int32, B, "lens"),
@@ -251,7 +254,8 @@ def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=k.device)
+        # zero-filled: each half begins with the scale kernel's counter
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
     _check(lib.wa_kv_quant_fp8_kv(_ptr(k), _act_strides(k), _ptr(v), _act_strides(v), B, H, T, D,

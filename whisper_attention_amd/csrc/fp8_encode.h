@@ -76,6 +76,29 @@ template <Fp8 F = Fp8::E4M3> __device__ __forceinline__ uint2 encode8_fast(uint4
   return pack8<F>(y);
 }
 
+// The quotient of quot_fast without its clamps, for a dynamic scale: every
+// value encoded with s = fp32(amax / FMAX) has |x| <= amax, so |x| * r and
+// the corrected quotient stay within FMAX (1 + 2^-22) -- no step can
+// overflow, and a quotient a rounding above FMAX still converts to the
+// largest code, as the clamped one does.
+template <Fp8 F> __device__ __forceinline__ float quot_dyn(float x, float s, float r) {
+  const float a = fabsf(x);
+  const float q0 = a * r;
+  const float e = __builtin_fmaf(-q0, s, a);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+
+template <Fp8 F = Fp8::E4M3> __device__ __forceinline__ uint2 encode8_dyn(uint4 v, float s, float r) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = quot_dyn<F>(bf16_lo(w[i]), s, r);
+    y[2 * i + 1] = quot_dyn<F>(bf16_hi(w[i]), s, r);
+  }
+  return pack8<F>(y);
+}
+
 __device__ __forceinline__ bool fast_scale(float s) { return s >= 0x1p-80f && s <= 0x1p80f; }
 
 // x / s encoded, by whichever quotient path the scale allows (the two give

@@ -12,18 +12,19 @@
 // at once and thread i always owns piece i % P: its head -- its scale group
 // -- never changes, and the 8 lanes of one head sit side by side in a wave.
 // Block (b, c) handles rows [c*R, (c+1)*R) of sequence b clipped to lens[b]
-// (R = rows_per_pass * loads per thread); every load of a thread is issued
-// before the first is used.  Wider rows (P > 1024) fall back to 1024 threads
-// that loop over pieces.
+// (R = rows_per_pass * rows per thread).  Wider rows (P > 1024) fall back to
+// 1024 threads that loop over pieces.
 //
 //   kv_amax_kernel      max of (bits & 0x7fff) per thread -- an exact,
 //                       order-free integer max equal to the fp32 abs-max of
 //                       the bf16 values -- folded over the 8 lanes of a head
 //                       (or the whole wave) and in LDS, one partial per block
-//                       and group, stored group-major.
-//   kv_scale_kernel     one block per group folds that group's partials and
-//                       writes scale[g] = amax_g / FMAX (1 when amax_g is 0),
-//                       FMAX = 448 (E4M3) or 57344 (E5M2).
+//                       and group, stored group-major.  Then each block takes
+//                       a ticket from a device-scope counter; the block that
+//                       draws the last one folds every partial and writes
+//                       scale[g] = amax_g / FMAX (1 when amax_g is 0), FMAX =
+//                       448 (E4M3) or 57344 (E5M2), and sets the counter back
+//                       to zero.  No block waits for another.
 //   kv_encode_kernel    divides each value by scale[g] (IEEE fp32 division),
 //                       clamps to +-FMAX, converts pairs with the hardware OCP
 //                       fp8/bf8 conversion (round to nearest even) and writes
@@ -36,8 +37,17 @@
 namespace wa {
 namespace {
 
-constexpr int kAmaxLoads = 8;    // rows per thread in the amax pass
+// Shapes measured on the prefill fill (K and V, 128 prompts, 20 heads):
+// 64 rows per amax block (two batches of 16 loads per thread) keeps the
+// partials few enough that the last block folds a group's 512 of them in one
+// batch of loads; 16-row blocks (1792 partials a group) made the fold alone
+// take ~30 us.
+constexpr int kAmaxBatch = 16;   // loads in flight per thread in the amax pass
+constexpr int kAmaxBatches = 2;  // batches per thread
+constexpr int kAmaxLoads = kAmaxBatch * kAmaxBatches;
 constexpr int kEncLoads = 4;     // rows per thread in the encode pass
+constexpr int kFoldBatch = 32;   // partial loads in flight per lane in the fold
+constexpr int kTicketWords = 64; // the per-tensor workspace starts with the ticket counter (256 bytes)
 
 __device__ __forceinline__ uint32_t maxabs_bits8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -76,13 +86,16 @@ __device__ __forceinline__ Lane lane_of(int P, int rows_per_pass) {
   return l;
 }
 
-// blockIdx.z picks the tensor (K or V of a pair call; 0 for one tensor).
+// blockIdx.z picks the tensor (K or V of a pair call; 0 for one tensor).  The
+// tensor's workspace is ws + z * ws_words: the ticket counter in word 0, the
+// partials from word kTicketWords, group-major.
 __global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_max, int P,
                                                        int rows_per_pass,
                                                        const int32_t *__restrict__ lens,
-                                                       int per_head, int groups,
-                                                       uint32_t *__restrict__ partial) {
+                                                       int per_head, int groups, uint32_t *ws,
+                                                       long ws_words, float fmax) {
   extern __shared__ uint32_t smax[];  // [groups]
+  __shared__ int s_last;
   const int b = blockIdx.x;
   const uint16_t *__restrict__ x = qt.x[blockIdx.z];
   const wa_strides xs = qt.xs[blockIdx.z];
@@ -98,15 +111,22 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_ma
   for (int p = ln.piece; p < P; p += (rows_per_pass > 0 ? P : step)) {
     const uint16_t *xp = x + (long)b * xs.b + (long)(p >> 3) * xs.h + (p & 7) * 8;
     uint32_t m = 0;
-    if (ln.active) {
-      uint4 v[kAmaxLoads];
+    if (ln.active && t0 + ln.row < t1) {
+      // rows past the end re-read the last valid row, which leaves a max
+      // unchanged; one batch of loads in flight at a time
+#pragma unroll 1
+      for (int bt = 0; bt < kAmaxBatches; ++bt) {
+        const int tb = t0 + ln.row + bt * kAmaxBatch * rpp;
+        if (tb >= t1) break;
+        uint4 v[kAmaxBatch];
 #pragma unroll
-      for (int u = 0; u < kAmaxLoads; ++u) {
-        const int t = t0 + ln.row + u * rpp;
-        v[u] = t < t1 ? *reinterpret_cast<const uint4 *>(xp + (long)t * xs.t) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kAmaxBatch; ++u) {
+          const int t = min(tb + u * rpp, t1 - 1);
+          v[u] = *reinterpret_cast<const uint4 *>(xp + (long)t * xs.t);
+        }
+#pragma unroll
+        for (int u = 0; u < kAmaxBatch; ++u) m = max(m, maxabs_bits8(v[u]));
       }
-#pragma unroll
-      for (int u = 0; u < kAmaxLoads; ++u) m = max(m, maxabs_bits8(v[u]));
     }
     // the 8 lanes of one head are adjacent and 8-aligned (P is a multiple of 8)
     m = max(m, (uint32_t)__shfl_xor((int)m, 1));
@@ -116,41 +136,55 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_ma
     if (rows_per_pass > 0) break;
   }
   __syncthreads();
-  uint32_t *pz = partial + (long)blockIdx.z * groups * n_blocks;
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) pz[(long)g * n_blocks + blk] = smax[g];
-}
-
-// One block per group (and tensor, blockIdx.z): fold that group's n_blocks
-// partials (contiguous).
-__global__ __launch_bounds__(256) void kv_scale_kernel(const uint32_t *__restrict__ partial,
-                                                       int n_blocks, float fmax, QuantTensors qt) {
-  __shared__ uint32_t wmax[4];
-  const int g = blockIdx.x;
-  float *__restrict__ scale = qt.scale[blockIdx.z];
-  const uint32_t *pg = partial + ((long)blockIdx.z * gridDim.x + g) * n_blocks;
-  // Every load of a pass is in flight at once: the partials were written on
-  // other XCDs, so each read is a full memory round trip (a group of the
-  // prompt prefill has 1792 partials: one pass of seven loads per thread).
-  uint32_t m = 0;
-  for (int j0 = threadIdx.x; j0 < n_blocks; j0 += 256 * 8) {
-    uint32_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = j0 + u * 256 < n_blocks ? pg[j0 + u * 256] : 0u;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = max(m, v[u]);
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  uint32_t *wz = ws + (long)blockIdx.z * ws_words;
+  uint32_t *pz = wz + kTicketWords;
+  // Publish the partials, then take a ticket; the block that draws the last
+  // one folds them all.  Everything another block reads -- the partials, the
+  // counter -- is written and read with agent-scope atomic operations, which
+  // the XCDs' L2 caches do not hold back (they are not coherent with each
+  // other); each partial store is complete (its vmcnt drained) before this
+  // block's barrier and so before its ticket, and the last block reads the
+  // partials after its ticket returned.  An agent-scope fence would do the
+  // same by writing back and invalidating a whole L2 in every block.
+  for (int g = threadIdx.x; g < groups; g += blockDim.x)
+    __hip_atomic_store(&pz[(long)g * n_blocks + blk], smax[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t a = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    const float amax = __uint_as_float(a << 16);  // bf16 bits -> fp32, exact
-    scale[g] = amax == 0.0f ? 1.0f : amax / fmax;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(wz, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(n_blocks - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // lanes per group: the largest power of two, at most a wave, that gives
+  // every group a slice of its own when the block is wide enough
+  int L = 64;
+  while (L > 1 && L * groups > (int)blockDim.x) L >>= 1;
+  const int li = threadIdx.x % L;
+  float *__restrict__ scale = qt.scale[blockIdx.z];
+  const int n = (int)n_blocks;
+  for (int g = threadIdx.x / L; g < groups; g += blockDim.x / L) {
+    const uint32_t *pg = pz + (long)g * n_blocks;
+    uint32_t mg = 0;
+    for (int i0 = li; i0 < n; i0 += L * kFoldBatch) {
+      uint32_t v[kFoldBatch];
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u)
+        v[u] = __hip_atomic_load(&pg[min(i0 + u * L, n - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u) mg = max(mg, v[u]);
+    }
+    for (int o = 1; o < L; o <<= 1) mg = max(mg, (uint32_t)__shfl_xor((int)mg, o, L));
+    if (li == 0) {
+      const float amax = __uint_as_float(mg << 16);  // bf16 bits -> fp32, exact
+      scale[g] = amax == 0.0f ? 1.0f : amax / fmax;
+    }
   }
+  // every ticket of this call is drawn: the next call starts from zero
+  if (threadIdx.x == 0) __hip_atomic_store(wz, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <Fp8 F>
+// kDyn: the scales were just computed from these values (no element exceeds
+// its group's amax), so the reciprocal quotient needs no clamp.
+template <Fp8 F, bool kDyn>
 __global__ __launch_bounds__(1024) void kv_encode_kernel(
     QuantTensors qt, int T_max, int P, int rows_per_pass, const int32_t *__restrict__ lens,
     const int32_t *__restrict__ dst_start, wa_strides cs, int cache_len, int per_head) {
@@ -184,7 +218,9 @@ __global__ __launch_bounds__(1024) void kv_encode_kernel(
 #pragma unroll
       for (int u = 0; u < kEncLoads; ++u) {
         const int t = t0 + ln.row + u * rpp;
-        if (t >= ta && t < tb) *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) = encode8_fast<F>(v[u], s, r);
+        if (t >= ta && t < tb)
+          *reinterpret_cast<uint2 *>(cp + (long)t * cs.t) =
+              kDyn ? encode8_dyn<F>(v[u], s, r) : encode8_fast<F>(v[u], s, r);
       }
     } else {
 #pragma unroll
@@ -225,7 +261,7 @@ QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran) {
 }
 
 size_t quant_workspace_bytes(const QuantPlan &p) {
-  const size_t n = (size_t)p.blocks * p.groups * sizeof(uint32_t);
+  const size_t n = kTicketWords * sizeof(uint32_t) + (size_t)p.blocks * p.groups * sizeof(uint32_t);
   return (n + 255) & ~(size_t)255;
 }
 
@@ -236,18 +272,16 @@ hipError_t launch_kv_quant(const QuantTensors &qt, int n_tensors, int B, int H, 
   (void)H;
   if (compute_scale) {
     const size_t lds = (size_t)plan.groups * sizeof(uint32_t);
+    const float fmax = fmt == Fp8::E4M3 ? fp8_max<Fp8::E4M3>() : fp8_max<Fp8::E5M2>();
     hipLaunchKernelGGL(kv_amax_kernel, dim3(B, plan.amax_chunks, n_tensors), dim3(plan.threads), lds,
                        stream, qt, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, per_head,
-                       plan.groups, ws);
+                       plan.groups, ws, (long)(quant_workspace_bytes(plan) / sizeof(uint32_t)), fmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const float fmax = fmt == Fp8::E4M3 ? fp8_max<Fp8::E4M3>() : fp8_max<Fp8::E5M2>();
-    hipLaunchKernelGGL(kv_scale_kernel, dim3(plan.groups, 1, n_tensors), dim3(256), 0, stream, ws,
-                       (int)plan.blocks, fmax, qt);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  auto kernel = fmt == Fp8::E4M3 ? kv_encode_kernel<Fp8::E4M3> : kv_encode_kernel<Fp8::E5M2>;
+  auto kernel = fmt == Fp8::E4M3
+                    ? (compute_scale ? kv_encode_kernel<Fp8::E4M3, true> : kv_encode_kernel<Fp8::E4M3, false>)
+                    : (compute_scale ? kv_encode_kernel<Fp8::E5M2, true> : kv_encode_kernel<Fp8::E5M2, false>);
   hipLaunchKernelGGL(kernel, dim3(B, plan.enc_chunks, n_tensors), dim3(plan.threads), 0, stream, qt,
                      T_max, plan.pieces_per_row, plan.rows_per_pass, lens, dst_start, cs, cache_len,
                      per_head);
