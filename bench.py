@@ -30,6 +30,7 @@ idle; the JSON line records how many (settle_steps).
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -286,7 +287,7 @@ class DecodeLayers:
                                 device=dev)
 
 
-def decode_step_graph(wa, d, iters=10):
+def decode_step_graph(wa, d, iters=10, reps=5):
     """A decode step over the decoder's layers: per layer the self-attention
     step with its append, then the cross-attention on the self output, launched
     eagerly and as one HIP graph."""
@@ -302,8 +303,6 @@ def decode_step_graph(wa, d, iters=10):
                               workspace=d.ws_x)
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         t0 = time.perf_counter()
         ev[0].record()
@@ -313,7 +312,8 @@ def decode_step_graph(wa, d, iters=10):
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) * 1e3 / iters, (time.perf_counter() - t0) * 1e6 / iters
 
-    eager_gpu, eager_wall = timed(step)
+    step()
+    torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -323,9 +323,21 @@ def decode_step_graph(wa, d, iters=10):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    graph_gpu, graph_wall = timed(graph.replay)
-    return {"layers": d.layers, "B": d.B, "eager_us": round(eager_wall, 1), "graph_us": round(graph_wall, 1),
-            "eager_gpu_us": round(eager_gpu, 1), "graph_gpu_us": round(graph_gpu, 1)}
+    graph.replay()
+    torch.cuda.synchronize()
+    # eager and captured runs alternate, so clock and cache drift over the
+    # measurement falls on both alike; the medians over the repetitions are
+    # reported
+    runs = {"eager": [], "graph": []}
+    for _ in range(reps):
+        runs["eager"].append(timed(step))
+        runs["graph"].append(timed(graph.replay))
+    med = {k: (statistics.median(g for g, _ in v), statistics.median(w for _, w in v)) for k, v in runs.items()}
+    return {"layers": d.layers, "B": d.B, "reps": reps, "eager_us": round(med["eager"][1], 1),
+            "graph_us": round(med["graph"][1], 1), "eager_gpu_us": round(med["eager"][0], 1),
+            "graph_gpu_us": round(med["graph"][0], 1),
+            "eager_gpu_us_runs": [round(g, 1) for g, _ in runs["eager"]],
+            "graph_gpu_us_runs": [round(g, 1) for g, _ in runs["graph"]]}
 
 
 def decode_steps_graph(wl, g_seed):
@@ -340,7 +352,8 @@ def decode_steps_graph(wl, g_seed):
     torch.cuda.synchronize()
     return {"B64": decode_step_graph(wa, big), "B1": decode_step_graph(wa, one),
             "note": "microseconds per 32-layer decode step (append + self, then cross, per layer): wall "
-                    "clock per step over the loop (host launch cost included) and GPU event time"}
+                    "clock per step over the loop (host launch cost included) and GPU event time, medians "
+                    "over alternating eager and captured runs"}
 
 
 def codec_rates(wl, steps):
