@@ -47,9 +47,11 @@
 // lanes it returns 4 keys x 1 dim per lane from 4 rows x 16 dims.
 //
 // Softmax: online, in the exp2 domain (softmax_scale * log2(e) folded into one
-// FMA per score), with a lazy rescale -- the running max moves only when a
-// tile max exceeds it by more than 2^8 -- and row sums of the bf16 weights
-// taken on the matrix pipe by a small 16x16x32 MFMA per key chunk.
+// FMA per score), against a running reference that is not the exact max: a
+// tile's weights are taken against it first, and only a weight of 2 or more
+// sends the tile through the exact max and a rescale (new_max below), so the
+// common tile spends no vector work on its max.  Row sums of the bf16 weights
+// are taken on the matrix pipe by a small 16x16x32 MFMA per key chunk.
 //
 // fp8 Q and K (kFp8, the aggressive-fp8 variant): E4M3 codes with
 // dequantization scales.  K tiles are 4 KB (64-byte rows) and S^T comes from
@@ -81,7 +83,7 @@ constexpr int kMaxCopies = 2;
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kTileBytes = kBN * 64 * 2;  // one 64 x 64 bf16 tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;             // lazy-rescale threshold, log2 units
+constexpr float kHeadroom = 8.0f;         // running max above the tile max, log2 units
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8): wait until at most N vector-memory operations of
 // this wave are outstanding and all its LDS operations are complete.
@@ -305,14 +307,10 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2][kNQ], const flo
   }
 }
 
-// Mask and tile max of one tile's scores, and the lazy-rescale decision:
-// the running max moves only when some query's tile max exceeds it by more
-// than kLazy (P then stays below 2^kLazy, which the bf16 weights and fp32
-// sums carry exactly as well).  Returns whether it moved; alpha[qb] is then
-// the factor that takes O and l from the old frame to the new one.
+// Scores of keys at or past the key length, and (causal) of keys after the
+// query, to -inf.  Only the last tile and the causal diagonal tiles have any.
 template <bool kCausal>
-__device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][kNQ], int k0, int len,
-                                         int wq_lo, float c_log2, int lane, float (&alpha)[kNQ]) {
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2][kNQ], int k0, int len, int wq_lo, int lane) {
   const int half = lane >> 5, col = lane & 31;
   if (k0 + kBN > len || (kCausal && k0 + kBN - 1 > wq_lo)) {
 #pragma unroll
@@ -331,8 +329,24 @@ __device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][kNQ], int
         }
     }
   }
-  float mt[kNQ];
-  bool moved = false;
+}
+
+// The running max (exp2 domain) is a reference point, not the exact max:
+// softmax is unchanged by a common shift of a row's scores, and the fp32 / bf16
+// weights and sums carry any shift that keeps the largest weight well inside
+// their range.  Each tile's weights are therefore first taken against the
+// running max as it stands; only when one of them reaches 2 (or is not
+// finite) is the tile redone: its exact max is taken, the running max moves
+// to kHeadroom above it, and O and the row sums are rescaled.  Afterwards the
+// tile's largest weight is 2^-kHeadroom, so the reference stays put until a
+// score exceeds the max seen so far by more than kHeadroom + 1.
+//
+// Tile max of the (masked) scores; moves the running max of each query to
+// kHeadroom above it when that is higher, and returns in alpha[qb] the factor
+// that takes O and l from the old frame to the new one (0 on the first tile,
+// 1 where the max stays).
+__device__ __forceinline__ void new_max(WaveState &st, const f32x16 (&s)[2][kNQ], float c_log2,
+                                        float (&alpha)[kNQ]) {
 #pragma unroll
   for (int qb = 0; qb < kNQ; ++qb) {
     float mx = -INFINITY;
@@ -340,17 +354,25 @@ __device__ __forceinline__ bool tile_max(WaveState &st, f32x16 (&s)[2][kNQ], int
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-    mt[qb] = max_with_lane_xor32(mx) * c_log2;
-    moved = moved || mt[qb] > st.m_run[qb] + kLazy;
-  }
-  if (__builtin_amdgcn_ballot_w64(moved) == 0) return false;
-#pragma unroll
-  for (int qb = 0; qb < kNQ; ++qb) {
-    const float m_new = fmaxf(st.m_run[qb], mt[qb]);
-    alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);   // 0 on the first tile
+    const float mt = max_with_lane_xor32(mx) * c_log2 + kHeadroom;
+    const float m_new = fmaxf(st.m_run[qb], mt);
+    alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
     st.m_run[qb] = m_new;
   }
-  return true;
+}
+
+// Whether any weight of the tile, as packed bf16 P^T operands, is 2 or more,
+// inf or NaN: the top exponent bit of a non-negative bf16 is set exactly then.
+__device__ __forceinline__ bool weight_reaches_two(const bf16x8 (&pb)[kNQ][4]) {
+  uint32_t acc = 0;
+#pragma unroll
+  for (int qb = 0; qb < kNQ; ++qb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 u = __builtin_bit_cast(uint4, pb[qb][c]);
+      acc |= u.x | u.y | u.z | u.w;
+    }
+  return __builtin_amdgcn_ballot_w64((acc & 0x40004000u) != 0) != 0;
 }
 
 // O and the row sums from the old frame to the new one (after a tile max
@@ -458,19 +480,38 @@ __device__ __forceinline__ void interval(WaveState &st, bf16x8 (&pa)[kNQ][4], co
   if (wave_needs<kCausal>(t - 1, x)) accumulate_pv(st, prev, x.ro, pa);
   if (wave_needs<kCausal>(t, x)) {
     f32x16 s[2][kNQ];
-    scores<kFp8>(st, cur, x.ro, s);
-    __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
-    float alpha[kNQ];
-    if (tile_max<kCausal>(st, s, t * kBN, x.len, x.wq_lo, x.c_log2, x.lane, alpha))
-      rescale(st, alpha, x.lane);
-    // An exponential costs two to four times the issue time of an FMA; the
-    // scheduling groups interleave them with the FMAs and conversions,
-    // which then issue in their shadow instead of before them.
-    softmax_exp(s, st.m_run, x.c_log2, pa);
+    // tile 0 is the first of every wave: it sets the running max
+    bool redo = t == 0;
+    if (!redo) {
+      scores<kFp8>(st, cur, x.ro, s);
+      __builtin_amdgcn_sched_barrier(0);  // matrix phase, then vector phase
+      mask_tile<kCausal>(s, t * kBN, x.len, x.wq_lo, x.lane);
+      softmax_exp(s, st.m_run, x.c_log2, pa);
+      // An exponential costs two to four times the issue time of an FMA; the
+      // scheduling groups interleave them with the FMAs and conversions,
+      // which then issue in their shadow instead of before them.
 #pragma unroll
-    for (int g = 0; g < 32 * kNQ; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
+      for (int g = 0; g < 32 * kNQ; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // one exponential
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two other vector ops
+      }
+      redo = weight_reaches_two(pa);
+    }
+    if (redo) {
+      // The scores are read again from LDS (tile t's K slot is not reused
+      // before the next interval) rather than kept: the weights overwrite
+      // them in place.  The opaque offsets keep the compiler from reusing
+      // the first reads.
+      ReadOffsets ro = x.ro;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(ro.k[c]));
+      asm volatile("" : "+v"(ro.k8[0]), "+v"(ro.k8[1]));
+      scores<kFp8>(st, cur, ro, s);
+      mask_tile<kCausal>(s, t * kBN, x.len, x.wq_lo, x.lane);
+      float alpha[kNQ];
+      new_max(st, s, x.c_log2, alpha);
+      rescale(st, alpha, x.lane);
+      softmax_exp(s, st.m_run, x.c_log2, pa);
     }
   }
 }
