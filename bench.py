@@ -52,10 +52,11 @@ N_SETS = 3                    # decode cache sets used in turn
 # code_hash) of the kernel source they were taken on: a changed kernel
 # reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("4ad2c9d38cc12360", {"encoder": 246.84e6, "prefill": 148.39e6,
-                                              "fp8qk_30s": 185.16e6, "prefill_cross": 1055.46e6}),
+    "encoder_attn.hip": ("204ffd2cc30ed751", {"encoder": 247.12e6, "prefill": 148.41e6,
+                                              "fp8qk_30s": 185.51e6, "prefill_cross": 1055.60e6}),
     "decode_attn.hip": ("c6eb9e4527d97166", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("3ee61d3727638963", {"cross": 368.68e6}),
+    "kv_quant.hip": ("4225e0144fcb30c7", {"pair": 185.96e6}),
 }
 
 
@@ -849,7 +850,10 @@ def main():
                          "frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4), "us": round(ms[0] * 1e3, 2)},
         "kv_quant": {"value": round(quant_gbps, 1), "unit": "GB/s",
                      "frac": round(quant_gbps / PEAK_HBM_GBPS, 4), "us": round(ms[1] * 1e3, 2),
-                     "note": "one wa_kv_quant_fp8_kv call (K and V): amax + scale + encode kernels"},
+                     "traffic": traffic("kv_quant.hip", "pair"), "algorithmic_bytes": wl.quant_bytes(),
+                     "note": "one wa_kv_quant_fp8_kv call (K and V): the amax kernel (its last block "
+                             "folds the scales) and the encode kernel; the encode re-reads the inputs "
+                             "(the traffic over the algorithmic bytes)"},
         **codecs,
         "per_call_us": {"in_step": dist, "decode_alone": ddist,
                         "note": "per-call event times over the timed steps: mean, median, p10, p90"},
