@@ -102,6 +102,28 @@ def test_ragged_edges(gpu, B, H, L):
         assert torch.all(got[torch.as_tensor(zero, device="cuda")].float() == 0)
 
 
+@pytest.mark.parametrize("B,H,L", [(8, 4, 300), (2, 2, 1500)])
+def test_every_finite_code(gpu, B, H, L):
+    """Caches of uniform random bytes over all 254 finite E4M3 codes: both
+    signs, zeros, the subnormals and every binade reach the in-register
+    dequantization (the bell-curve caches of the other tests sit in the top
+    binades).  (2, 2, 1500) takes the split-key path and its merge."""
+    import whisper_attention_amd as wa
+    announce(f"decode every finite E4M3 code B={B} H={H} L={L}")
+    g = np.random.default_rng(L + B)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    kc = torch.from_numpy(finite[g.integers(0, finite.size, size=(B, H, L, 64))])
+    vc = torch.from_numpy(finite[g.integers(0, finite.size, size=(B, H, L, 64))])
+    # dequantized magnitudes up to 448 * 0.01
+    ks = g.uniform(0.005, 0.01, size=H).astype(np.float32)
+    vs = g.uniform(0.005, 0.01, size=H).astype(np.float32)
+    lens = g.integers(1, L + 1, size=B)
+    lens[0] = L
+    q = torch.from_numpy(g.standard_normal((B, H, 64)).astype(np.float32)).to(torch.bfloat16)
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens, "head"), f"decode every code B={B} H={H} L={L}")
+
+
 def test_strided_cache_with_guards(gpu):
     """Caches that are slices of a larger buffer: padding slots hold NaN codes
     that must never be read."""
