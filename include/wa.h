@@ -116,7 +116,8 @@ typedef struct {
  * workspace  device scratch of at least wa_kv_quant_fp8_workspace_size()
  *            bytes (only used when compute_scale = 1; may be NULL otherwise).
  *            Its first 256 bytes hold a counter through which the last of
- *            the scale kernel's blocks finds itself; it must be zero before
+ *            the amax pass's blocks finds itself (that block folds the
+ *            scales); it must be zero before
  *            the first call that uses the workspace (a zero-filled
  *            allocation), and every call leaves it zero again, so a
  *            workspace reused call after call needs no further clearing.

@@ -201,7 +201,7 @@ def test_head_counts_and_block_shapes(gpu, H):
 
 def test_dynamic_scale_long_rows_one_head(gpu):
     """A dynamic scale over 139001 rows of one head: a large grid of amax
-    blocks, so the scale kernel folds thousands of partials per group."""
+    blocks, so the last amax block folds thousands of partials per group."""
     import whisper_attention_amd as wa
     B, T, H = 2, 70000, 1
     announce(f"quant dynamic scale, B={B} T={T} H={H} (many partials)")

@@ -223,7 +223,7 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
-        # zero-filled: the workspace begins with the scale kernel's counter
+        # zero-filled: the workspace begins with the scale fold's counter
         workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ng = 1 if g == WA_SCALE_PER_TENSOR else H
@@ -254,7 +254,7 @@ def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3
     g = _gran(gran)
     if workspace is None and compute_scale:
         n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
-        # zero-filled: each half begins with the scale kernel's counter
+        # zero-filled: each half begins with the scale fold's counter
         workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ng = 1 if g == WA_SCALE_PER_TENSOR else H

@@ -6,7 +6,7 @@
 //
 // One block = 4 waves = 128 queries of one (b, h); each wave owns one
 // 32-query MFMA column block and walks the keys in tiles of 64.  A wave takes
-// 122 VGPRs and a block 40 KB of LDS, so four blocks share a CU (one wave of
+// at most 128 VGPRs and a block 40 KB of LDS, so four blocks share a CU (one wave of
 // each on every SIMD): while one wave's matrix work runs, the others' vector
 // work and waits fill the SIMD.  (64 queries per wave, two column blocks per
 // K and V fragment read, needs 218 VGPRs and so allows two blocks per CU: 5 %
