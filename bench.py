@@ -520,6 +520,23 @@ def mfma_ceilings():
     return res
 
 
+def sclk_after_encoder(wl, n=10):
+    """The shader clock read by a short probe launched right after each of n
+    encoder calls (MHz, mean).  The clock recovers within microseconds of
+    the encoder's end, so this is the clock around the kernel, not inside it
+    (inside it, timestamps from s_memtime against s_memrealtime read ~1.5 GHz
+    on this workload)."""
+    try:
+        from whisper_attention_amd import diag
+    except ImportError:
+        return None
+    probe = diag.SclkProbe(n_blocks=8, spin=300)
+    for _ in range(n):
+        wl.wa.wa_encoder_attn(wl.qe, wl.ke, wl.ve, out=wl.oe, softmax_scale=0.125)
+        probe.launch()
+    return probe.mhz()
+
+
 def fill_caches(wa, B, H, L, lens, gran, g):
     """K and V E4M3 caches [B][H][L][64] with dynamic scales, filled by the
     quantize kernel from N(0,1) bf16 (untimed)."""
@@ -786,6 +803,7 @@ def main():
     enc_fp8 = encoder_fp8qk(args.steps, g_seed=3)
     xpre = cross_prefill(args.steps, g_seed=4)
     ceiling = mfma_ceilings()
+    ceiling["sclk_after_encoder_MHz"] = sclk_after_encoder(wl)
     graph_step = None if args.no_graph else decode_steps_graph(wl, g_seed=2)
     codecs = codec_rates(wl, args.steps)
     if args.copy_calib:

@@ -42,6 +42,23 @@ wa_status wa_diag_mfma_ceiling(wa_diag_dtype dtype, int n_blocks, int iters, uin
                                hipStream_t stream);
 
 /*
+ * wa_diag_sclk_probe -- the shader clock right now.
+ *
+ * What: n_blocks blocks of one wave; each reads the shader clock
+ *   (s_memtime) and the 100 MHz constant clock (s_memrealtime) while it
+ *   spins for `spin` constant-clock ticks (bounded by a read count as well,
+ *   so it always ends).  Launched on `stream` right after a kernel, it reads
+ *   the clock that kernel left the GPU at: the power management changes it
+ *   over much longer times than the probe takes (a spin of 500 is 5 us).
+ * ticks      device uint64 [n_blocks][2]: shader-clock cycles and
+ *            constant-clock ticks of each block's spin; their ratio times
+ *            wa_diag_wall_clock_khz is the shader clock.
+ * Errors: null ticks, n_blocks outside [1, 2^16] or spin outside [1, 10^5]
+ *   -> WA_ERR_INVALID_ARGUMENT; a launch failure -> WA_ERR_HIP.
+ */
+wa_status wa_diag_sclk_probe(int n_blocks, int spin, uint64_t *ticks, hipStream_t stream);
+
+/*
  * wa_diag_wall_clock_khz -- the rate of the constant clock that
  * s_memrealtime counts on the current device, in kHz, into *khz (host).
  * Errors: null khz -> WA_ERR_INVALID_ARGUMENT; HIP failure -> WA_ERR_HIP.

@@ -313,6 +313,10 @@ def test_diag_library_exports_and_validates():
     assert diag.lib.wa_diag_mfma_ceiling(0, 0, 16, FAKE, None) == 1
     assert diag.lib.wa_diag_mfma_ceiling(1, 512, (1 << 20) + 1, FAKE, None) == 1
     assert diag.lib.wa_diag_wall_clock_khz(None) == 1
+    assert diag.lib.wa_diag_sclk_probe(8, 500, None, None) == 1
+    assert diag.lib.wa_diag_sclk_probe(0, 500, FAKE, None) == 1
+    assert diag.lib.wa_diag_sclk_probe(8, 0, FAKE, None) == 1
+    assert diag.lib.wa_diag_sclk_probe(8, 100001, FAKE, None) == 1
 
 
 @pytest.mark.parametrize("lang,std", [("c", "-std=c11"), ("c++", "-std=c++17")])

@@ -17,3 +17,13 @@ def test_mfma_ceiling_probe(gpu, dtype, peak):
     assert r["wall_clock_kHz"] > 0
     assert r["sclk_MHz"] is not None and 100.0 < r["sclk_MHz"] < 3000.0
     assert 0.0 < r["TFLOP/s"] <= 1.05 * peak * r["sclk_MHz"] / 2400.0
+
+
+def test_sclk_probe(gpu):
+    """The clock probe reads a plausible shader clock and ends on its own."""
+    from whisper_attention_amd import diag
+    p = diag.SclkProbe(n_blocks=8, spin=200)
+    for _ in range(3):
+        p.launch()
+    mhz = p.mhz()
+    assert mhz is not None and 100.0 < mhz < 3000.0

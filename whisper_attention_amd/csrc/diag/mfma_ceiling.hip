@@ -60,9 +60,36 @@ __global__ __launch_bounds__(256) void mfma_ceiling_kernel(int iters, uint64_t *
   }
 }
 
+// One wave per block reads the shader clock (s_memtime) and the constant
+// clock (s_memrealtime) over a spin of `spin` constant-clock ticks; the loop
+// also ends after max_iters reads, so it ends even if the constant clock
+// stood still.
+__global__ __launch_bounds__(64) void sclk_probe_kernel(int spin, int max_iters, uint64_t *ticks) {
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t t0 = clock64(), r0 = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);
+  uint64_t r1 = r0;
+  for (int i = 0; i < max_iters && r1 - r0 < (uint64_t)spin; ++i) r1 = wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t t1 = clock64();
+  if (threadIdx.x == 0) {
+    ticks[2 * blockIdx.x] = t1 - t0;
+    ticks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+wa_status wa_diag_sclk_probe(int n_blocks, int spin, uint64_t *ticks, hipStream_t stream) {
+  if (!ticks || n_blocks < 1 || n_blocks > (1 << 16) || spin < 1 || spin > 100000)
+    return WA_ERR_INVALID_ARGUMENT;
+  // one constant-clock read per iteration: 64 reads per tick leave the spin
+  // the deciding condition at any clock rate this probe is for
+  hipLaunchKernelGGL(sclk_probe_kernel, dim3(n_blocks), dim3(64), 0, stream, spin, spin * 64, ticks);
+  return hipGetLastError() == hipSuccess ? WA_OK : WA_ERR_HIP;
+}
 
 wa_status wa_diag_mfma_ceiling(wa_diag_dtype dtype, int n_blocks, int iters, uint64_t *ticks,
                                hipStream_t stream) {

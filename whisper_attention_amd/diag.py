@@ -20,13 +20,15 @@ def _load():
     lib.wa_diag_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                          ctypes.c_void_p]
     lib.wa_diag_mfma_ceiling.restype = ctypes.c_int
+    lib.wa_diag_sclk_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.wa_diag_sclk_probe.restype = ctypes.c_int
     lib.wa_diag_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
     lib.wa_diag_wall_clock_khz.restype = ctypes.c_int
     return lib
 
 
 lib = _load()
-EXPORTED = ("wa_diag_mfma_ceiling", "wa_diag_wall_clock_khz")
+EXPORTED = ("wa_diag_mfma_ceiling", "wa_diag_sclk_probe", "wa_diag_wall_clock_khz")
 
 
 def mfma_ceiling(dtype="bf16", blocks_per_cu=2, iters=4096, reps=10):
@@ -63,3 +65,36 @@ def mfma_ceiling(dtype="bf16", blocks_per_cu=2, iters=4096, reps=10):
     return {"TFLOP/s": round(flop / sec / 1e12, 1), "sclk_MHz": None if mhz is None else round(mhz, 0),
             "us_per_call": round(sec * 1e6, 1), "blocks": n_blocks, "iters": iters,
             "wall_clock_kHz": khz.value}
+
+
+class SclkProbe:
+    """The shader clock right after the work enqueued before it: ``launch()``
+    enqueues the probe on the current stream (no synchronization), ``mhz()``
+    synchronizes and returns the mean over its blocks of the measured
+    launches since the last read."""
+
+    def __init__(self, n_blocks=8, spin=500):
+        self.n_blocks, self.spin = n_blocks, spin
+        self.khz = ctypes.c_int(0)
+        if lib.wa_diag_wall_clock_khz(ctypes.byref(self.khz)) != 0:
+            raise RuntimeError("wa_diag_wall_clock_khz failed")
+        self.bufs, self.used = [], 0
+
+    def launch(self):
+        if self.used == len(self.bufs):
+            self.bufs.append(torch.zeros((self.n_blocks, 2), dtype=torch.int64, device="cuda"))
+        t = self.bufs[self.used]
+        self.used += 1
+        st = lib.wa_diag_sclk_probe(self.n_blocks, self.spin, t.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"wa_diag_sclk_probe returned {st}")
+
+    def mhz(self):
+        torch.cuda.synchronize()
+        vals = []
+        for t in self.bufs[:self.used]:
+            a = t.cpu().numpy().astype("float64")
+            ok = a[:, 1] > 0
+            vals.extend(list(a[ok, 0] / a[ok, 1] * self.khz.value / 1e3))
+        self.used = 0
+        return None if not vals else round(float(sum(vals) / len(vals)), 0)
