@@ -172,6 +172,27 @@ def test_late_large_scores(gpu, lam, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_redo_every_tile(gpu, causal):
+    """The keys of tile j scaled by 1 + 2.5 j: each tile's largest score
+    exceeds the previous tile's by more than the kernel's headroom above its
+    reference (8 log2 units), so nearly every tile's weights reach 2 against
+    the reference and the tile is redone with its exact max, rescaling O and
+    the row sums each time; the early tiles' weights end up below fp32's
+    range, as they are below the oracle's rounding.  Ragged last tile."""
+    import whisper_attention_amd as wa
+    B, H, T = 2, 3, 1500
+    announce(f"encoder rising scores, every tile redone, causal={causal}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=12)
+    kf = k.float()
+    for j in range((T + 63) // 64):
+        kf[:, j * 64:(j + 1) * 64] *= 1.0 + 2.5 * j
+    k = kf.to(torch.bfloat16)
+    lens = [1500, 1471]
+    got = _gpu(wa, q, k, v, lens, causal)
+    _check(got, q, k, v, lens, causal, f"rising scores causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_every_ring_position(gpu, causal):
     """Key ranges of 1 to 14 tiles, whole and ragged, in one batch: the loop
     over key tiles (two K slots, three V slots, unrolled by six) ends at
