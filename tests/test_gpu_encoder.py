@@ -154,9 +154,9 @@ def test_deterministic(gpu):
 def test_late_large_scores(gpu, lam, causal):
     """Keys of later tiles scaled by lam: the scores of those tiles exceed
     the earlier tiles' by about 4*lam bits (exp2 domain), so the running max
-    jumps in the middle of a row (and, for lam = 4, may stay within the lazy
-    rescale's 2^8 slack) -- in a full middle tile, in one key of an early
-    tile and in the ragged last tile."""
+    jumps in the middle of a row (and, for lam = 4, may stay within the
+    kernel's headroom above its reference, so no redo) -- in a full middle
+    tile, in one key of an early tile and in the ragged last tile."""
     import whisper_attention_amd as wa
     B, H, T = 2, 2, 700
     announce(f"encoder late large scores lam={lam} causal={causal}")
