@@ -6,15 +6,16 @@
 //
 // One block = 4 waves = 128 queries of one (b, h); each wave owns one
 // 32-query MFMA column block and walks the keys in tiles of 64.  A wave takes
-// at most 128 VGPRs and a block 40 KB of LDS, so four blocks share a CU (one wave of
-// each on every SIMD): while one wave's matrix work runs, the others' vector
-// work and waits fill the SIMD.  (64 queries per wave, two column blocks per
-// K and V fragment read, needs 216 VGPRs and so allows two blocks per CU: no
-// faster on the 30-s encoder, 5 % slower on the 15-s window, 22 % on the 10-s
-// window and 14 % on the prompt prefill.)  A non-causal query range of 129 to 256 rows (a prompt attending
-// to the encoder frames) takes one block of eight waves per (b, h) instead,
-// so that K and V are copied from memory once rather than by two blocks
-// that drift apart and miss in L2.
+// at most 128 VGPRs and a block 40 KB of LDS, so four blocks share a CU (one
+// wave of each on every SIMD): while one wave's matrix work runs, the others'
+// vector work and waits fill the SIMD.  (64 queries per wave, two column
+// blocks per K and V fragment read, needs 216 VGPRs and so allows two blocks
+// per CU: no faster on the 30-s encoder, 5 % slower on the 15-s window, 22 %
+// on the 10-s window and 14 % on the prompt prefill.)  A non-causal query
+// range of 129 to 256 rows (a prompt attending to the encoder frames) takes
+// one block of eight waves per (b, h) instead, so that K and V are copied
+// from memory once rather than by two blocks that drift apart and miss in
+// L2.
 //
 // Both products run on v_mfma_f32_32x32x16_bf16 in transposed form, so the
 // accumulator's lane index is the query:
