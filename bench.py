@@ -641,8 +641,42 @@ def tiny(steps, g_seed):
                                                    workspace=ws_s),
     }
     res = {name: dist_us(time_calls(fn, steps)) for name, fn in legs.items()}
+    for name, fn in legs.items():
+        res[name]["graph_us"] = graph_per_call_us(fn)
     res["config"] = f"B={B} H={H}: encoder T={T}; decode cross {T} + self {Ls}, per-tensor E4M3"
+    res["note"] = ("mean/median/p10/p90: event time per eager call, which at this size includes the host's "
+                   "launch cost; graph_us: GPU time per call of 20 calls captured in one HIP graph, median "
+                   "of 5 replays")
     return res
+
+
+def graph_per_call_us(fn, n=20, reps=5):
+    """GPU time per call (µs) of ``n`` calls of ``fn`` captured in one HIP
+    graph: the median over ``reps`` replays, each bracketed by events."""
+    fn(0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / n)
+    del graph
+    return round(statistics.median(per), 2)
 
 
 def cpu_baseline(budget_s):
