@@ -59,6 +59,45 @@ def test_ragged_shapes(gpu, B, H, T, lens, causal):
     _check(got, q, k, v, lens, causal, f"encoder B={B} H={H} T={T} causal={causal}")
 
 
+# Key lengths around the tile edges (64 keys) and around where two key groups
+# split a sequence's tiles (the first group takes ceil(tiles / 2)).
+EDGE_LENS = [1, 64, 65, 128, 129, 192, 255, 256, 257, 300]
+
+
+def test_two_key_groups_at_tile_edges(gpu):
+    """A grid of few blocks (B*H*query tiles <= 256, 256 keys or more) runs
+    two key groups per block, merged in LDS: every key length around a tile
+    edge and around the groups' split point, all rows."""
+    import whisper_attention_amd as wa
+    B, H, T = len(EDGE_LENS), 2, 300
+    announce(f"encoder two key groups B={B} H={H} T={T} lens={EDGE_LENS}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=31)
+    got = _gpu(wa, q, k, v, EDGE_LENS, False)
+    _check(got, q, k, v, EDGE_LENS, False, "encoder two key groups")
+
+
+def test_one_key_group_at_tile_edges(gpu):
+    """The same key lengths on a grid large enough (576 blocks) for one key
+    group per block, all rows."""
+    import whisper_attention_amd as wa
+    B, H, T = 24, 8, 300
+    lens = [EDGE_LENS[i % len(EDGE_LENS)] for i in range(B)]
+    announce(f"encoder one key group B={B} H={H} T={T}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=32)
+    got = _gpu(wa, q, k, v, lens, False)
+    _check(got, q, k, v, lens, False, "encoder one key group")
+
+
+def test_single_chunk_large_v3_all_rows(gpu):
+    """One 30-s chunk of the large-v3 shape (B=1, 20 heads, 240 query tiles:
+    two key groups per block), every row."""
+    import whisper_attention_amd as wa
+    announce("encoder B=1 H=20 T=1500")
+    q, k, v = workloads.encoder_inputs(1, 20, 1500, seed=33)
+    got = _gpu(wa, q, k, v, None, False)
+    _check(got, q, k, v, None, False, "encoder B=1 H=20")
+
+
 def test_small_workload(gpu):
     import whisper_attention_amd as wa
     cfg = workloads.CONFIGS["tiny"]

@@ -65,6 +65,20 @@ def _check(got, qc, qs, kc, ks, v, lens, causal, gran, what, pairs=None):
     assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what, mag=np.concatenate(ms))
 
 
+def test_two_key_groups_at_tile_edges(gpu):
+    """Few blocks, so two key groups per block (merged in LDS), per-head
+    scales; key lengths around the tile edges and the groups' split point."""
+    import whisper_attention_amd as wa
+    lens = [1, 64, 65, 128, 129, 192, 255, 256, 257, 300]
+    B, H, T = len(lens), 2, 300
+    announce(f"fp8qk two key groups B={B} H={H} T={T} lens={lens}")
+    q, k, v = workloads.encoder_inputs(B, H, T, seed=34)
+    qc, qs = _codes(q, lens, "head")
+    kc, ks = _codes(k, lens, "head")
+    got = _run(wa, qc, qs, kc, ks, v, lens, False, "head")
+    _check(got, qc, qs, kc, ks, v, lens, False, "head", "fp8qk two key groups")
+
+
 @pytest.mark.parametrize("gran", ["tensor", "head"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,T,lens", [(2, 3, 300, [300, 131]), (3, 2, 77, [77, 1, 64]), (1, 1, 1, [1]),

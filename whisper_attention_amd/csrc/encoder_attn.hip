@@ -153,6 +153,10 @@ __device__ __forceinline__ uint32_t copy_offset_k8(wa_strides ks, int max_row, i
 // tile uses the first half of its slot).
 __shared__ __attribute__((aligned(1024))) uint8_t g_kring[2][kTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_vring[3][kTileBytes];
+// The second key group's rings (two-group blocks only): K slots 0-1, then V
+// slots 0-2, in one array so that after the loop the 40 KB also carry the
+// group's partial results to the first group.
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring1[5][kTileBytes];
 
 // One asynchronous 16-byte-per-lane copy global -> LDS: lane l's 16 bytes,
 // read from base + voff, land at LDS byte address lds + 16*l.  Written out
@@ -170,13 +174,13 @@ __device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t voff, u
 }
 
 // LDS byte addresses of a K or V slot, as the instruction's M0 wants them.
-__device__ __forceinline__ uint32_t k_addr(int slot) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_kring[0][0] +
-         slot * kTileBytes;
+__device__ __forceinline__ uint32_t k_addr(int slot, bool g1) {
+  const uint8_t *base = g1 ? &g_ring1[0][0] : &g_kring[0][0];
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)base + slot * kTileBytes;
 }
-__device__ __forceinline__ uint32_t v_addr(int slot) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&g_vring[0][0] +
-         slot * kTileBytes;
+__device__ __forceinline__ uint32_t v_addr(int slot, bool g1) {
+  const uint8_t *base = g1 ? &g_ring1[2][0] : &g_vring[0][0];
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)base + slot * kTileBytes;
 }
 
 // Issue the asynchronous copy of the K/V tile that starts at row k0 into K
@@ -188,21 +192,21 @@ template <bool kFp8, int kW>
 __device__ __forceinline__ void issue_tile(int kslot, int vslot, const void *kp, wa_strides ks,
                                            const uint16_t *vp, wa_strides vs, int k0, int kend,
                                            const CopyOffsets (&full)[kMaxCopies], uint32_t k8, int lane,
-                                           int w) {
+                                           int w, bool g1) {
   constexpr int kC = kCopiesOf<kW>;
 #pragma unroll
   for (int i = 0; i < kC; ++i) {
     const int row0 = (w * kC + i) * 8;
     // only the last tile can run past kend
     const CopyOffsets c = k0 + kBN <= kend ? full[i] : copy_offsets(ks, vs, kend - 1 - k0, lane, row0);
-    const uint32_t dst = k_addr(kslot) + row0 * 128;
+    const uint32_t dst = k_addr(kslot, g1) + row0 * 128;
     if (!kFp8) copy16_to_lds(static_cast<const uint16_t *>(kp) + (long)k0 * ks.t, c.k, dst);
-    copy16_to_lds(vp + (long)k0 * vs.t, c.v, v_addr(vslot) + row0 * 128);
+    copy16_to_lds(vp + (long)k0 * vs.t, c.v, v_addr(vslot, g1) + row0 * 128);
   }
   if (kFp8 && w < 4) {  // four 16-row copies fill a 4 KB fp8 K tile
     const int row0 = w * 16;
     const uint32_t off = k0 + kBN <= kend ? k8 : copy_offset_k8(ks, kend - 1 - k0, lane, row0);
-    copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, k_addr(kslot) + row0 * 64);
+    copy16_to_lds(static_cast<const uint8_t *>(kp) + (long)k0 * ks.t, off, k_addr(kslot, g1) + row0 * 64);
   }
 }
 
@@ -442,6 +446,7 @@ struct Ctx {
   ReadOffsets ro;
   int nt, kend, len, wq_lo, lane, w;
   float c_log2;
+  bool g1;     // the block's second key group (two-group blocks), else false
 };
 
 // Interval t: K of tile t is in `cur`, V of tile t-1 in `prev`; tile t+1 is
@@ -462,7 +467,8 @@ __device__ __forceinline__ void open_interval(int kahead, int vahead, int t, con
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   if (t + 1 < x.nt)
-    issue_tile<kFp8, kW>(kahead, vahead, x.kp, x.ks, x.vp, x.vs, (t + 1) * kBN, x.kend, x.co, x.k8, x.lane, x.w);
+    issue_tile<kFp8, kW>(kahead, vahead, x.kp, x.ks, x.vp, x.vs, (t + 1) * kBN, x.kend, x.co, x.k8, x.lane, x.w,
+                         x.g1);
 }
 
 // causal: a wave whose every query precedes every key of tile j skips it
@@ -531,8 +537,16 @@ __device__ __forceinline__ void zero_rows(uint16_t *o, wa_strides os, int b, int
 // dequantization scales q_scale / k_scale ([1], or [H] when per_head).
 // Queries i < q_lens[b] (of Tq_max rows) attend keys j < k_lens[b] (of Tk_max
 // rows); the causal form needs both to be the same sequence.
-template <bool kCausal, bool kFp8, int kW>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(
+//
+// kG = 2 (non-causal, for grids too small to fill the GPU): the block holds
+// two groups of kW waves over the same queries.  The first takes the first
+// ceil(n/2) key tiles, the second the rest, each with its own rings, under
+// the one barrier per interval; at the end the second group hands its
+// running max, row sums and unnormalized O to the first through LDS, which
+// combines the two as the split-key merge does (each weighted by 2 to the
+// power of its max less the larger max) and writes the output.
+template <bool kCausal, bool kFp8, int kW, int kG>
+__global__ __launch_bounds__(kW * kG * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_kernel(
     const void *__restrict__ q, wa_strides qs, const void *__restrict__ k, wa_strides ks,
     const uint16_t *__restrict__ v, wa_strides vs, uint16_t *__restrict__ o, wa_strides os, int H,
     int Tq_max, const int32_t *__restrict__ q_lens, int Tk_max, const int32_t *__restrict__ k_lens,
@@ -558,17 +572,32 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave within its key group (read as a scalar: the group is wave-uniform)
+  const int wv = kG == 1 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = kG == 1 ? wv : wv % kW;
   const int half = lane >> 5, col = lane & 31;
   Ctx x;
-  x.kp = kFp8 ? (const void *)(static_cast<const uint8_t *>(k) + (long)b * ks.b + (long)h * ks.h)
-              : (const void *)(static_cast<const uint16_t *>(k) + (long)b * ks.b + (long)h * ks.h);
-  x.vp = v + (long)b * vs.b + (long)h * vs.h;
+  x.g1 = kG == 2 && wv >= kW;
+  // this group's keys: [k_lo, k_lo + len_g)
+  int k_lo = 0, len_g = len_k, n0 = 0;
+  if (kG == 2) {
+    n0 = ((len_k + kBN - 1) / kBN + 1) / 2;
+    k_lo = x.g1 ? n0 * kBN : 0;
+    len_g = x.g1 ? max(len_k - n0 * kBN, 0) : min(len_k, n0 * kBN);
+  }
+  x.kp = kFp8 ? (const void *)(static_cast<const uint8_t *>(k) + (long)b * ks.b + (long)h * ks.h +
+                               (long)k_lo * ks.t)
+              : (const void *)(static_cast<const uint16_t *>(k) + (long)b * ks.b + (long)h * ks.h +
+                               (long)k_lo * ks.t);
+  x.vp = v + (long)b * vs.b + (long)h * vs.h + (long)k_lo * vs.t;
   x.ks = ks;
   x.vs = vs;
-  x.kend = kCausal ? min(len_k, q0 + kBM) : len_k;
+  x.kend = kCausal ? min(len_k, q0 + kBM) : len_g;
   x.nt = (x.kend + kBN - 1) / kBN;
-  x.len = len_k;
+  x.len = len_g;
+  // intervals 0 .. nloop: both groups pass the same barriers
+  const int nloop = kG == 1 ? x.nt : n0;
   x.wq_lo = q0 + w * kQW;
   x.lane = lane;
   x.w = w;
@@ -579,13 +608,17 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int i = 0; i < kCopiesOf<kW>; ++i)
     x.co[i] = copy_offsets(ks, vs, kBN - 1, lane, (w * kCopiesOf<kW> + i) * 8);
   x.k8 = copy_offset_k8(ks, kBN - 1, lane, w * 16);
-  issue_tile<kFp8, kW>(0, 0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w);
+  if (kG == 1 || x.nt > 0) issue_tile<kFp8, kW>(0, 0, x.kp, ks, x.vp, vs, 0, x.kend, x.co, x.k8, lane, w, x.g1);
   x.ro = read_offsets(lane);
   if (x.wq_lo >= len) {
     // Every query of this wave lies past the query length (short prompts in
     // a query tile): it does its share of the copies and passes the same
     // barriers as the other waves, and computes nothing.
-    for (int t = 0; t <= x.nt; ++t) open_interval<kFp8, kW>((t + 1) & 1, (t + 1) % 3, t, x);
+    for (int t = 0; t <= nloop; ++t) open_interval<kFp8, kW>((t + 1) & 1, (t + 1) % 3, t, x);
+    if (kG == 2) {
+      __builtin_amdgcn_s_barrier();  // the two barriers of the groups' hand-over
+      __builtin_amdgcn_s_barrier();
+    }
     return;
   }
 
@@ -624,18 +657,26 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   // intervals t = 0 .. nt: tile t's K and tile t-1's V; K of tile j is in K
   // slot j % 2, V of tile j in V slot j % 3
   bf16x8 pa[kNQ][4];
-  for (int t = 0; t <= x.nt; t += 6) {
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[2], 1, 1, t, x);
-    if (t + 1 > x.nt) break;
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[0], 0, 2, t + 1, x);
-    if (t + 2 > x.nt) break;
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[1], 1, 0, t + 2, x);
-    if (t + 3 > x.nt) break;
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[2], 0, 1, t + 3, x);
-    if (t + 4 > x.nt) break;
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[0], g_vring[0], 1, 2, t + 4, x);
-    if (t + 5 > x.nt) break;
-    interval<kCausal, kFp8, kW>(st, pa, g_kring[1], g_vring[1], 0, 0, t + 5, x);
+  const uint8_t *K0 = g_kring[0], *K1 = g_kring[1], *V0 = g_vring[0], *V1 = g_vring[1], *V2 = g_vring[2];
+  if (kG == 2 && x.g1) {
+    K0 = g_ring1[0];
+    K1 = g_ring1[1];
+    V0 = g_ring1[2];
+    V1 = g_ring1[3];
+    V2 = g_ring1[4];
+  }
+  for (int t = 0; t <= nloop; t += 6) {
+    interval<kCausal, kFp8, kW>(st, pa, K0, V2, 1, 1, t, x);
+    if (t + 1 > nloop) break;
+    interval<kCausal, kFp8, kW>(st, pa, K1, V0, 0, 2, t + 1, x);
+    if (t + 2 > nloop) break;
+    interval<kCausal, kFp8, kW>(st, pa, K0, V1, 1, 0, t + 2, x);
+    if (t + 3 > nloop) break;
+    interval<kCausal, kFp8, kW>(st, pa, K1, V2, 0, 1, t + 3, x);
+    if (t + 4 > nloop) break;
+    interval<kCausal, kFp8, kW>(st, pa, K0, V0, 1, 2, t + 4, x);
+    if (t + 5 > nloop) break;
+    interval<kCausal, kFp8, kW>(st, pa, K1, V1, 0, 0, t + 5, x);
   }
 
 #pragma unroll
@@ -644,7 +685,38 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     // row sum of query col: element 0 (col < 16) or 1 (col >= 16) of lane col%16
     const float l0 = __shfl(st.lacc[qb][0], col & 15, 64);
     const float l1 = __shfl(st.lacc[qb][1], col & 15, 64);
-    const float l_tot = col < 16 ? l0 : l1;
+    float l_tot = col < 16 ? l0 : l1;
+    if constexpr (kG == 2) {
+      // The hand-over: once every wave is past its last ring read, the
+      // second group's wave w stores its max, row sum and O (column-major by
+      // lane, 34 words a lane) in the second rings' memory, and the first
+      // group's wave w, which holds the same queries, takes them in.
+      static_assert(kNQ == 1 && kW * 34 * 64 * 4 <= 5 * kTileBytes, "hand-over buffer");
+      float *xb = reinterpret_cast<float *>(&g_ring1[0][0]) + w * (34 * 64);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (x.g1) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * 64 + lane] = st.oacc[db][qb][r];
+        xb[32 * 64 + lane] = st.m_run[qb];
+        xb[33 * 64 + lane] = l_tot;
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0Lgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (x.g1) return;
+      const float m0 = st.m_run[qb], m1 = xb[32 * 64 + lane];
+      const float mx = fmaxf(m0, m1);
+      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mx);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+      l_tot = a0 * l_tot + a1 * xb[33 * 64 + lane];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st.oacc[db][qb][r] = a0 * st.oacc[db][qb][r] + a1 * xb[(db * 16 + r) * 64 + lane];
+    }
     if (my_q < len) {
       const float inv = 1.0f / l_tot;
       uint16_t *op = o + (long)b * os.b + (long)my_q * os.t + (long)h * os.h;
@@ -677,11 +749,20 @@ hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_stride
   const int bm = wide ? kBMOf<8> : kBMOf<4>;
   const int n_qt = (Tq_max + bm - 1) / bm;
   const long total = (long)B * H * n_qt;
-  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block((wide ? 8 : 4) * 64);
+  // Two key groups per block when the grid has no more blocks than the chip
+  // has CUs and there are keys enough to share: the same blocks, twice the
+  // waves, half the intervals.  (Measured: the single 30-s chunk of 20 heads
+  // 25.8 -> 22.0 us, 6 heads 23.7 -> 19.4 us; at 384 and 480 blocks no
+  // change, so those keep one group.  With so few waves an interval waits
+  // mostly on its tile copy, which is why halving the intervals does not
+  // halve the time.)
+  const bool split = !causal && !wide && total <= 256 && Tk_max >= 4 * kBN;
+  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block((wide || split ? 8 : 4) * 64);
   const bool fp8 = q_scale != nullptr;
-  auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true, 4> : attn_fwd_kernel<true, false, 4>)
-                       : wide ? (fp8 ? attn_fwd_kernel<false, true, 8> : attn_fwd_kernel<false, false, 8>)
-                              : (fp8 ? attn_fwd_kernel<false, true, 4> : attn_fwd_kernel<false, false, 4>);
+  auto kernel = causal ? (fp8 ? attn_fwd_kernel<true, true, 4, 1> : attn_fwd_kernel<true, false, 4, 1>)
+                : wide ? (fp8 ? attn_fwd_kernel<false, true, 8, 1> : attn_fwd_kernel<false, false, 8, 1>)
+                : split ? (fp8 ? attn_fwd_kernel<false, true, 4, 2> : attn_fwd_kernel<false, false, 4, 2>)
+                        : (fp8 ? attn_fwd_kernel<false, true, 4, 1> : attn_fwd_kernel<false, false, 4, 1>);
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, qs, k, ks, v, vs, o, os, H, Tq_max, q_lens,
                      Tk_max, k_lens, c_log2, q_scale, k_scale, per_head, n_qt, (int)total);
   return hipGetLastError();
