@@ -52,7 +52,7 @@ N_SETS = 3                    # decode cache sets used in turn
 # code_hash) of the kernel source they were taken on: a changed kernel
 # reports null.
 TRAFFIC = {
-    "encoder_attn.hip": ("204ffd2cc30ed751", {"encoder": 247.12e6, "prefill": 148.41e6,
+    "encoder_attn.hip": ("e8c76f65a8ae475b", {"encoder": 247.29e6, "prefill": 148.40e6,
                                               "fp8qk_30s": 185.51e6, "prefill_cross": 1055.60e6}),
     "decode_attn.hip": ("c6eb9e4527d97166", {"cross": 246.21e6, "self": 42.13e6}),
     "kv_dequant.hip": ("3ee61d3727638963", {"cross": 368.68e6}),
