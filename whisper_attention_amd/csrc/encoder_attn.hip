@@ -753,9 +753,10 @@ hipError_t launch_encoder(const void *q, wa_strides qs, const void *k, wa_stride
   // has CUs and there are keys enough to share: the same blocks, twice the
   // waves, half the intervals.  (Measured: the single 30-s chunk of 20 heads
   // 25.8 -> 22.0 us, 6 heads 23.7 -> 19.4 us; at 384 and 480 blocks no
-  // change, so those keep one group.  With so few waves an interval waits
-  // mostly on its tile copy, which is why halving the intervals does not
-  // halve the time.)
+  // change, so those keep one group; four groups gained nothing over two.
+  // The waves of one block keep their matrix and vector phases together
+  // under its barrier, so more waves in a block overlap little of their
+  // work.)
   const bool split = !causal && !wide && total <= 256 && Tk_max >= 4 * kBN;
   const dim3 grid((unsigned)((total + 7) / 8 * 8)), block((wide || split ? 8 : 4) * 64);
   const bool fp8 = q_scale != nullptr;
