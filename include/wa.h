@@ -129,7 +129,11 @@ wa_status wa_kv_quant_fp8(const uint16_t *x, wa_strides xs, int B, int H, int T_
                           wa_scale_gran gran, int compute_scale, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
-size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gran);
+/* Workspace bytes for one tensor of wa_kv_quant_fp8 (and _fmt) at batch B,
+ * H heads and scale granularity gran: a 256-byte counter and the amax pass's
+ * partial maxima, at most 32 per sequence and scale group whatever the
+ * sequence length.  0 for B <= 0, H <= 0 or an unknown gran. */
+size_t wa_kv_quant_fp8_workspace_size(int B, int H, wa_scale_gran gran);
 
 /*
  * wa_kv_quant_fp8_fmt -- wa_kv_quant_fp8 with the float8 format chosen.

@@ -43,9 +43,12 @@ def test_status_strings(wa):
 
 
 def test_workspace_sizes(wa):
-    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, 224, "head") > 0
-    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, 224, "tensor") > 0
-    assert wa.wa_kv_quant_fp8_workspace_size(0, 20, 224, "head") == 0
+    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, "head") > 0
+    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, "tensor") > 0
+    assert wa.wa_kv_quant_fp8_workspace_size(0, 20, "head") == 0
+    # the counter plus at most 32 partials per sequence and scale group
+    assert wa.wa_kv_quant_fp8_workspace_size(128, 20, "head") == 256 + 128 * 32 * 20 * 4
+    assert wa.wa_kv_quant_fp8_workspace_size(3, 20, "tensor") == 768   # 256 + 3 * 32 * 4, rounded up to 256
     assert wa.wa_decode_attn_workspace_size(1, 6, 1500) > 0      # split keys -> partials
     assert wa.wa_decode_attn_workspace_size(0, 6, 1500) == 0
     # a big batch needs no split, hence no workspace
@@ -123,7 +126,7 @@ def test_quant_pair_validation(wa):
     assert call(D=32) == wa.WA_ERR_UNSUPPORTED
     assert call(vs=_S(wa, t=20 * 64 + 4)) == wa.WA_ERR_UNSUPPORTED
     # the workspace holds two tensors' partials
-    one = wa.wa_kv_quant_fp8_workspace_size(2, 20, 1500, "tensor")
+    one = wa.wa_kv_quant_fp8_workspace_size(2, 20, "tensor")
     assert call(wsb=one) == wa.WA_ERR_WORKSPACE_TOO_SMALL
 
 

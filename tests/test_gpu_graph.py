@@ -132,7 +132,7 @@ def test_captured_prompt_step_equals_eager(gpu):
     vc = torch.zeros_like(kc)
     ks = torch.zeros(H, dtype=torch.float32, device="cuda")
     vs = torch.zeros_like(ks)
-    half = wa.wa_kv_quant_fp8_workspace_size(B, H, T, "head")
+    half = wa.wa_kv_quant_fp8_workspace_size(B, H, "head")
     ws = torch.zeros(2 * half, dtype=torch.uint8, device="cuda")
     o_p, o_x = torch.empty_like(q), torch.empty_like(q)
     o_e = torch.empty_like(qe)

@@ -67,7 +67,7 @@ def _load():
     lib.wa_kv_quant_fp8_kv.restype = I
     lib.wa_kv_dequant_fp8.argtypes = [P, S, I, P, I, I, P, I, I, I, I, P, S, P]
     lib.wa_kv_dequant_fp8.restype = I
-    lib.wa_kv_quant_fp8_workspace_size.argtypes = [I, I, I, I]
+    lib.wa_kv_quant_fp8_workspace_size.argtypes = [I, I, I]
     lib.wa_kv_quant_fp8_workspace_size.restype = Z
     lib.wa_encoder_attn.argtypes = [P, S, P, S, P, S, P, S, I, I, I, I, P, I, F, P]
     lib.wa_encoder_attn.restype = I
@@ -190,8 +190,8 @@ def _same_device(ref, *ts):
             raise ValueError(f"every tensor must be on {ref.device}; got one on {t.device}")
 
 
-def wa_kv_quant_fp8_workspace_size(B, H, T_max, gran):
-    return int(lib.wa_kv_quant_fp8_workspace_size(B, H, T_max, _gran(gran)))
+def wa_kv_quant_fp8_workspace_size(B, H, gran):
+    return int(lib.wa_kv_quant_fp8_workspace_size(B, H, _gran(gran)))
 
 
 def wa_decode_attn_workspace_size(B, H, cache_len):
@@ -222,7 +222,7 @@ def wa_kv_quant_fp8_fmt(x, cache, scale, gran, fmt, lens=None, dst_start=None, c
     _same_device(x, cache, scale, lens, dst_start, workspace)
     g = _gran(gran)
     if workspace is None and compute_scale:
-        n = wa_kv_quant_fp8_workspace_size(B, H, T, g)
+        n = wa_kv_quant_fp8_workspace_size(B, H, g)
         # zero-filled: the workspace begins with the scale fold's counter
         workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -253,7 +253,7 @@ def wa_kv_quant_fp8_kv(k, v, k_cache, v_cache, k_scale, v_scale, gran, fmt="e4m3
     _same_device(k, v, k_cache, v_cache, k_scale, v_scale, lens, dst_start, workspace)
     g = _gran(gran)
     if workspace is None and compute_scale:
-        n = 2 * wa_kv_quant_fp8_workspace_size(B, H, T, g)
+        n = 2 * wa_kv_quant_fp8_workspace_size(B, H, g)
         # zero-filled: each half begins with the scale fold's counter
         workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=k.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

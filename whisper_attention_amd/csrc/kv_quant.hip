@@ -48,6 +48,10 @@ constexpr int kAmaxLoads = kAmaxBatch * kAmaxBatches;
 constexpr int kEncLoads = 4;     // rows per thread in the encode pass
 constexpr int kFoldBatch = 32;   // partial loads in flight per lane in the fold
 constexpr int kTicketWords = 64; // the per-tensor workspace starts with the ticket counter (256 bytes)
+// Amax blocks per sequence at most (a longer sequence's blocks stride over
+// its row chunks), so that the partials, and the workspace, do not grow with
+// the sequence length: 32 chunks of 64 rows cover 2048 positions at 20 heads.
+constexpr int kMaxAmaxChunks = 32;
 
 __device__ __forceinline__ uint32_t maxabs_bits8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -100,8 +104,8 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_ma
   const uint16_t *__restrict__ x = qt.x[blockIdx.z];
   const wa_strides xs = qt.xs[blockIdx.z];
   const int rpp = max(rows_per_pass, 1);
-  const int t0 = blockIdx.y * rpp * kAmaxLoads;
-  const int t1 = min(t0 + rpp * kAmaxLoads, seq_len(lens, b, T_max));
+  const int rows_blk = rpp * kAmaxLoads;   // rows of one chunk
+  const int n_len = seq_len(lens, b, T_max);
   const long n_blocks = (long)gridDim.x * gridDim.y;
   const long blk = (long)blockIdx.y * gridDim.x + blockIdx.x;
   for (int g = threadIdx.x; g < groups; g += blockDim.x) smax[g] = 0;
@@ -111,7 +115,10 @@ __global__ __launch_bounds__(1024) void kv_amax_kernel(QuantTensors qt, int T_ma
   for (int p = ln.piece; p < P; p += (rows_per_pass > 0 ? P : step)) {
     const uint16_t *xp = x + (long)b * xs.b + (long)(p >> 3) * xs.h + (p & 7) * 8;
     uint32_t m = 0;
-    if (ln.active && t0 + ln.row < t1) {
+    // this block's row chunks: blockIdx.y, then every gridDim.y-th
+    for (int t0 = blockIdx.y * rows_blk; ln.active && t0 < n_len; t0 += gridDim.y * rows_blk) {
+      const int t1 = min(t0 + rows_blk, n_len);
+      if (t0 + ln.row >= t1) break;
       // rows past the end re-read the last valid row, which leaves a max
       // unchanged; one batch of loads in flight at a time
 #pragma unroll 1
@@ -254,14 +261,14 @@ QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran) {
     p.rows_per_pass = 0;    // threads loop over pieces, one row per pass
   }
   const int rpp = std::max(p.rows_per_pass, 1);
-  p.amax_chunks = (T_max + rpp * kAmaxLoads - 1) / (rpp * kAmaxLoads);
+  p.amax_chunks = std::min((T_max + rpp * kAmaxLoads - 1) / (rpp * kAmaxLoads), kMaxAmaxChunks);
   p.enc_chunks = (T_max + rpp * kEncLoads - 1) / (rpp * kEncLoads);
   p.blocks = (long)B * p.amax_chunks;
   return p;
 }
 
-size_t quant_workspace_bytes(const QuantPlan &p) {
-  const size_t n = kTicketWords * sizeof(uint32_t) + (size_t)p.blocks * p.groups * sizeof(uint32_t);
+size_t quant_workspace_bytes(int B, int groups) {
+  const size_t n = kTicketWords * sizeof(uint32_t) + (size_t)B * kMaxAmaxChunks * groups * sizeof(uint32_t);
   return (n + 255) & ~(size_t)255;
 }
 
@@ -275,7 +282,7 @@ hipError_t launch_kv_quant(const QuantTensors &qt, int n_tensors, int B, int H, 
     const float fmax = fmt == Fp8::E4M3 ? fp8_max<Fp8::E4M3>() : fp8_max<Fp8::E5M2>();
     hipLaunchKernelGGL(kv_amax_kernel, dim3(B, plan.amax_chunks, n_tensors), dim3(plan.threads), lds,
                        stream, qt, T_max, plan.pieces_per_row, plan.rows_per_pass, lens, per_head,
-                       plan.groups, ws, (long)(quant_workspace_bytes(plan) / sizeof(uint32_t)), fmax);
+                       plan.groups, ws, (long)(quant_workspace_bytes(B, plan.groups) / sizeof(uint32_t)), fmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -69,9 +69,10 @@ const char *wa_status_string(wa_status s) {
   return "unknown wa_status";
 }
 
-size_t wa_kv_quant_fp8_workspace_size(int B, int H, int T_max, wa_scale_gran gran) {
-  if (B <= 0 || H <= 0 || T_max <= 0) return 0;
-  return wa::quant_workspace_bytes(wa::quant_plan(B, H, T_max, gran));
+size_t wa_kv_quant_fp8_workspace_size(int B, int H, wa_scale_gran gran) {
+  if (B <= 0 || H <= 0) return 0;
+  if (gran != WA_SCALE_PER_TENSOR && gran != WA_SCALE_PER_HEAD) return 0;
+  return wa::quant_workspace_bytes(B, gran == WA_SCALE_PER_HEAD ? H : 1);
 }
 
 }  // extern "C"
@@ -101,7 +102,7 @@ wa_status quant_common(const uint16_t *k, wa_strides ks, const uint16_t *v, wa_s
   if (compute_scale) {
     if (!workspace) return WA_ERR_INVALID_ARGUMENT;
     if (!aligned16(workspace)) return WA_ERR_UNSUPPORTED;
-    if (workspace_bytes < n * wa::quant_workspace_bytes(plan)) return WA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < n * wa::quant_workspace_bytes(B, plan.groups)) return WA_ERR_WORKSPACE_TOO_SMALL;
   }
   wa_status st = check_device();
   if (st != WA_OK) return st;

@@ -29,12 +29,13 @@ struct QuantPlan {
   int groups;           // 1 (per tensor) or H (per head)
   int threads;          // threads per block
   int rows_per_pass;    // whole rows a block covers at once (0: threads loop over pieces)
-  int amax_chunks;      // amax blocks per sequence
+  int amax_chunks;      // amax blocks per sequence (at most 32; they stride over longer sequences)
   int enc_chunks;       // encode blocks per sequence
   long blocks;          // amax blocks in all (B * amax_chunks): partials per group
 };
 QuantPlan quant_plan(int B, int H, int T_max, wa_scale_gran gran);
-size_t quant_workspace_bytes(const QuantPlan &p);
+// per tensor: the counter and B * 32 partials per scale group, whatever T_max
+size_t quant_workspace_bytes(int B, int groups);
 
 // One or two tensors (K and V) that share shape, lengths, slots and the cache
 // layout; each has its own input, cache and scales.
@@ -44,7 +45,7 @@ struct QuantTensors {
   uint8_t *cache[2];
   float *scale[2];
 };
-// The workspace holds n_tensors * quant_workspace_bytes(plan) bytes.
+// The workspace holds n_tensors * quant_workspace_bytes(B, plan.groups) bytes.
 hipError_t launch_kv_quant(const QuantTensors &qt, int n_tensors, int B, int H, int T_max,
                            const int32_t *lens, const int32_t *dst_start, wa_strides cs,
                            int cache_len, int per_head, int compute_scale, Fp8 fmt, uint32_t *ws,
