@@ -98,6 +98,26 @@ def test_single_chunk_large_v3_all_rows(gpu):
     _check(got, q, k, v, None, False, "encoder B=1 H=20")
 
 
+def test_long_sequence_two_key_groups(gpu):
+    """4096 frames, 2 heads: 64 query tiles, so two key groups per block of
+    32 key tiles each (every ring slot many times over); all rows."""
+    import whisper_attention_amd as wa
+    announce("encoder long sequence B=1 H=2 T=4096")
+    q, k, v = workloads.encoder_inputs(1, 2, 4096, seed=35)
+    got = _gpu(wa, q, k, v, [4001], False)
+    _check(got, q, k, v, [4001], False, "encoder T=4096 two key groups")
+
+
+def test_long_sequence_one_key_group(gpu):
+    """4096 frames, 64 heads, B=2 (4096 blocks, one key group): two
+    sampled (b, h) checked in full."""
+    import whisper_attention_amd as wa
+    announce("encoder long sequence B=2 H=64 T=4096")
+    q, k, v = workloads.encoder_inputs(2, 64, 4096, seed=36)
+    got = _gpu(wa, q, k, v, [4096, 3970], False)
+    _check(got, q, k, v, [4096, 3970], False, "encoder T=4096 one key group", pairs=[(0, 0), (1, 63)])
+
+
 def test_small_workload(gpu):
     import whisper_attention_amd as wa
     cfg = workloads.CONFIGS["tiny"]
