@@ -49,6 +49,7 @@ def test_workspace_sizes(wa):
     # the counter plus at most 32 partials per sequence and scale group
     assert wa.wa_kv_quant_fp8_workspace_size(128, 20, "head") == 256 + 128 * 32 * 20 * 4
     assert wa.wa_kv_quant_fp8_workspace_size(3, 20, "tensor") == 768   # 256 + 3 * 32 * 4, rounded up to 256
+    assert wa.lib.wa_kv_quant_fp8_workspace_size(3, 20, 7) == 0          # no such granularity
     assert wa.wa_decode_attn_workspace_size(1, 6, 1500) > 0      # split keys -> partials
     assert wa.wa_decode_attn_workspace_size(0, 6, 1500) == 0
     # a big batch needs no split, hence no workspace
