@@ -102,6 +102,27 @@ def test_ragged_edges(gpu, B, H, L):
         assert torch.all(got[torch.as_tensor(zero, device="cuda")].float() == 0)
 
 
+def test_long_cache_many_chunks(gpu):
+    """A 100,000-slot cache for two (b, h) pairs: the keys split into
+    hundreds of chunks whose partials the merge kernel combines; ragged
+    lengths, per-head scales, all rows against the oracle, and the
+    no-allocation entry point on the same call."""
+    import whisper_attention_amd as wa
+    B, H, L = 1, 2, 100_000
+    lens = [99_937]
+    announce(f"decode long cache B={B} H={H} L={L} lens={lens}")
+    n_split = wa.wa_decode_attn_workspace_size(B, H, L) // (B * H * 68 * 4)
+    assert n_split > 100
+    q, kc, vc, ks, vs, lens = workloads.decode_inputs(B, H, L, lens, "head", 9, "self")
+    got = _gpu_decode(wa, q, kc, vc, ks, vs, lens, "head")
+    _close(got, _oracle(q, kc, vc, ks, vs, lens, "head"), "decode long cache")
+    again = torch.full_like(got, float("nan"))
+    wa.wa_decode_attn_noalloc(to_dev(q), to_dev(kc), to_dev(vc), to_dev(ks), to_dev(vs),
+                              to_dev(np.asarray(lens, np.int32)), "head", again, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), got.view(torch.int16))
+
+
 @pytest.mark.parametrize("B,H,L", [(8, 4, 300), (2, 2, 1500)])
 def test_every_finite_code(gpu, B, H, L):
     """Caches of uniform random bytes over all 254 finite E4M3 codes: both
