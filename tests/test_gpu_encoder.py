@@ -108,6 +108,16 @@ def test_long_sequence_two_key_groups(gpu):
     _check(got, q, k, v, [4001], False, "encoder T=4096 two key groups")
 
 
+def test_long_sequence_causal(gpu):
+    """A 3000-token causal prompt, 2 heads: 24 query tiles, each with its own
+    diagonal tile and up to 47 key tiles before it; all rows."""
+    import whisper_attention_amd as wa
+    announce("encoder causal long sequence B=1 H=2 T=3000")
+    q, k, v = workloads.encoder_inputs(1, 2, 3000, seed=37)
+    got = _gpu(wa, q, k, v, [2950], True)
+    _check(got, q, k, v, [2950], True, "encoder causal T=3000")
+
+
 def test_long_sequence_one_key_group(gpu):
     """4096 frames, 64 heads, B=2 (4096 blocks, one key group): two
     sampled (b, h) checked in full."""
