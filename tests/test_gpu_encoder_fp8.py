@@ -65,6 +65,19 @@ def _check(got, qc, qs, kc, ks, v, lens, causal, gran, what, pairs=None):
     assert_close(torch.from_numpy(np.concatenate(gs)), np.concatenate(ws), what, mag=np.concatenate(ms))
 
 
+def test_long_sequence(gpu):
+    """4096 frames, 2 heads, per-head scales (two key groups of 32 tiles),
+    all rows."""
+    import whisper_attention_amd as wa
+    lens = [4090]
+    announce("fp8qk long sequence B=1 H=2 T=4096")
+    q, k, v = workloads.encoder_inputs(1, 2, 4096, seed=38)
+    qc, qs = _codes(q, lens, "head")
+    kc, ks = _codes(k, lens, "head")
+    got = _run(wa, qc, qs, kc, ks, v, lens, False, "head")
+    _check(got, qc, qs, kc, ks, v, lens, False, "head", "fp8qk T=4096")
+
+
 def test_two_key_groups_at_tile_edges(gpu):
     """Few blocks, so two key groups per block (merged in LDS), per-head
     scales; key lengths around the tile edges and the groups' split point."""
