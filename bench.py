@@ -185,9 +185,9 @@ class Workload:
                     caches[name + kv] = (c, s)
                     del src
             self.sets.append(caches)
-        self.ws_dx = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)),
+        self.ws_dx = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)),
                                  dtype=torch.uint8, device=dev)
-        self.ws_ds = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)),
+        self.ws_ds = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)),
                                  dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -282,9 +282,9 @@ class DecodeLayers:
                         caches[name + kv] = (c, sc)
                 sets.append(caches)
         self.sets = sets
-        self.ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8,
+        self.ws_x = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8,
                                 device=dev)
-        self.ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8,
+        self.ws_s = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8,
                                 device=dev)
 
 
@@ -582,8 +582,8 @@ def decode_long(steps, g_seed):
             for _ in range(N_SETS)]
     q = gen_bf16((B, H, HEAD_DIM), g)
     o_x, o_s = torch.empty_like(q), torch.empty_like(q)
-    ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8, device="cuda")
-    ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, cap)), dtype=torch.uint8, device="cuda")
+    ws_x = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8, device="cuda")
+    ws_s = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, cap)), dtype=torch.uint8, device="cuda")
 
     def cross(i):
         (kc, ks), (vc, vs) = sets[i % N_SETS][0]
@@ -641,8 +641,8 @@ def tiny(steps, g_seed):
     o = torch.empty_like(q)
     lx = torch.full((B,), T, dtype=torch.int32, device="cuda")
     ls = torch.full((B,), Ls, dtype=torch.int32, device="cuda")
-    ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, T)), dtype=torch.uint8, device="cuda")
-    ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8, device="cuda")
+    ws_x = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, T)), dtype=torch.uint8, device="cuda")
+    ws_s = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8, device="cuda")
     legs = {
         "encoder": lambda i: wa.wa_encoder_attn(qe, ke, ve, out=oe, softmax_scale=0.125),
         "kv_quant_cross_k": lambda i: wa.wa_kv_quant_fp8(xk_src, xkc, xks, "tensor", workspace=ws_q),

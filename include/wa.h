@@ -307,8 +307,14 @@ wa_status wa_encoder_attn_fp8qk(const uint8_t *q, wa_strides qs, const float *q_
  * k_scale, v_scale  device float32 [1] or [H] (gran).
  * lens       device int32 [B] (required).
  * o          device bf16 [B][H][64]; os.b and os.h used.
- * workspace  device scratch of at least wa_decode_attn_workspace_size() bytes;
- *            needs no initialisation.
+ * workspace  device scratch of at least wa_decode_attn_workspace_size() bytes
+ *            (0 when the keys are not split; NULL is then allowed).  It
+ *            begins with one counter per (b, h), through which the last of a
+ *            pair's chunk blocks finds itself and merges the chunks, so the
+ *            workspace must be zero before the first call that uses it (a
+ *            zero-filled allocation); every call leaves the counters zero
+ *            again, so a workspace reused call after call needs no further
+ *            clearing.
  */
 wa_status wa_decode_attn(const uint16_t *q, wa_strides qs, const uint8_t *k_cache,
                          const uint8_t *v_cache, wa_strides cs, int cache_len,
@@ -355,12 +361,13 @@ wa_status wa_decode_attn_append(const uint16_t *q, wa_strides qs, const uint16_t
  * nothing; inputs, outputs and errors are those of wa_decode_attn (same
  * kernels, bit-identical results).
  *
- * The split-key partials go to a static device array of
+ * The split-key counters and partials go to a static device array of
  * WA_DECODE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
- * until the process ends.  A call whose partials (the bytes
- * wa_decode_attn_workspace_size reports) exceed it returns WA_ERR_TOO_LARGE
- * and launches nothing; with the current planner no call needs more than
- * about 452 KB.  Every call on a GPU shares that GPU's array: two calls in
+ * until the process ends (zero when the library loads; every call leaves
+ * its counters zero).  A call whose scratch (the bytes
+ * wa_decode_attn_workspace_size reports) exceeds it returns
+ * WA_ERR_TOO_LARGE and launches nothing; with the current planner no call
+ * needs more than about 455 KB.  Every call on a GPU shares that GPU's array: two calls in
  * flight at once on one GPU (on two streams, or from two host threads) race
  * and must not overlap.
  */

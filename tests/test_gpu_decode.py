@@ -104,7 +104,7 @@ def test_ragged_edges(gpu, B, H, L):
 
 def test_long_cache_many_chunks(gpu):
     """A 100,000-slot cache for two (b, h) pairs: the keys split into
-    hundreds of chunks whose partials the merge kernel combines; ragged
+    hundreds of chunks whose partials the last chunk block combines; ragged
     lengths, per-head scales, all rows against the oracle, and the
     no-allocation entry point on the same call."""
     import whisper_attention_amd as wa

@@ -76,8 +76,8 @@ def test_captured_decode_step_equals_eager(gpu, B, H):
     announce(f"decode step in a HIP graph: B={B} H={H}, 4 layers")
     Ls, Lx = 448, 1500
     lay = _layer_inputs(B, H, Ls, Lx, 4, 11)
-    ws_s = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8, device="cuda")
-    ws_x = torch.empty(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8, device="cuda")
+    ws_s = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Ls)), dtype=torch.uint8, device="cuda")
+    ws_x = torch.zeros(max(16, wa.wa_decode_attn_workspace_size(B, H, Lx)), dtype=torch.uint8, device="cuda")
     _step(wa, lay, ws_s, ws_x)                  # eager reference (also warms up)
     torch.cuda.synchronize()
     ref = [(L["o_s"].clone(), L["o_x"].clone(), L["kc"].clone(), L["vc"].clone()) for L in lay]

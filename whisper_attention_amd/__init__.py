@@ -375,7 +375,8 @@ def wa_decode_attn(q, k_cache, v_cache, k_scale, v_scale, lens, gran, softmax_sc
     _shape(out, (B, H, D), "out")
     if workspace is None:
         n = wa_decode_attn_workspace_size(B, H, L)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        # zero-filled: a split-key call's workspace begins with its counters
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
     _same_device(q, k_cache, v_cache, k_scale, v_scale, lens, out, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     g = _gran(gran)
@@ -410,7 +411,8 @@ def wa_decode_attn_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, l
     _shape(out, (B, H, D), "out")
     if workspace is None:
         n = wa_decode_attn_workspace_size(B, H, L)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        # zero-filled: a split-key call's workspace begins with its counters
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
     _same_device(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, lens, out, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     g = _gran(gran)

@@ -35,6 +35,13 @@ namespace {
 constexpr int kMaxWaves = 8;
 constexpr int kBlockKeys = 64;       // keys per wave iteration
 constexpr int kPartialStride = 68;   // o[64], m, l, pad
+// Split-key workspace: a fixed block of uint32 counters, one per (b, h),
+// then the partials.  The planner splits only below kSplitPairs (b, h)
+// pairs, so the counters always fit and always sit at the same place: a
+// workspace reused for calls of other shapes finds zeros there (every call
+// leaves its counters zero), never the partials of an earlier call.
+constexpr int kSplitPairs = 640;
+constexpr long kCounterWords = kSplitPairs;   // 2560 bytes
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaveSlots = 5120;     // resident waves: 256 CUs x 4 SIMDs x 5
 
@@ -87,6 +94,73 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Partials of split-key calls are stored and read with agent-scope atomic
+// operations: the blocks of one (b, h) run on different XCDs, whose L2
+// caches are not coherent with each other.
+__device__ __forceinline__ void store_partial(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float *p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Called by the one wave of a block that stored the block's partial: once
+// its stores are complete it draws a ticket from the (b, h)'s counter, and
+// the wave that draws the last of the n_split tickets combines the partials
+// (lane = output dim): with M the largest chunk max,
+// o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, times the value scale.
+// It then sets the counter back to zero.  No block waits for another.
+__device__ __forceinline__ void merge_if_last(uint32_t *cnt, const float *part, int BH, int bh,
+                                              int n_split, int lane, float vs_g, uint16_t *orow) {
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t t = 0;
+  if (lane == 0) t = __hip_atomic_fetch_add(&cnt[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  t = (uint32_t)__shfl((int)t, 0, 64);
+  if (t != (uint32_t)(n_split - 1)) return;
+  // lane i (and i + 64, ...) reads chunk i's max: the loads go out together
+  float M = -INFINITY;
+  for (int i = lane; i < n_split; i += 64)
+    M = fmaxf(M, load_partial(part + ((long)i * BH + bh) * kPartialStride + 64));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int i0 = 0; i0 < n_split; i0 += 64) {
+      // chunk i0 + lane's weight and sum, then each chunk's O, dim = lane
+      const int i = i0 + lane;
+      float e = 0.f, li = 0.f;
+      if (i < n_split) {
+        const float *pw = part + ((long)i * BH + bh) * kPartialStride;
+        const float mi = load_partial(pw + 64);
+        li = load_partial(pw + 65);
+        e = mi == -INFINITY ? 0.f : exp2f(mi - M);
+      }
+      den = fmaf(e, li, den);
+      const int n = min(64, n_split - i0);
+      for (int j0 = 0; j0 < n; j0 += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + u, n - 1);
+          ov[u] = load_partial(part + ((long)(i0 + j) * BH + bh) * kPartialStride + lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float ej = __shfl(e, min(j0 + u, n - 1), 64);
+          if (j0 + u < n) num = fmaf(ej, ov[u], num);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  }
+  const float out = den > 0.f ? num / den * vs_g : 0.f;
+  orow[lane] = f32_to_bf16(out);
+  if (lane == 0) __hip_atomic_store(&cnt[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // kAppend: the new token's K and V (bf16 k_new, v_new [B][H][64]) are
 // encoded with the stored scales into slot lens[b] - 1 of the caches and
 // attended to from registers; every other wave and block reads only the
@@ -105,6 +179,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int n_waves = blockDim.x >> 6;
   const int split = blockIdx.x % n_split;
   const int bh = blockIdx.x / n_split;
+  const int BH = gridDim.x / n_split;
+  // split-key calls: the workspace holds a counter per (b, h), then the partials
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(ws);
+  float *part = ws + kCounterWords;
   const int b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane >> 2, qd = lane & 3;
@@ -238,15 +316,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
         reinterpret_cast<uint4 *>(op)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         reinterpret_cast<uint4 *>(op)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
       } else {
-        float *pw = ws + ((long)split * (gridDim.x / n_split) + bh) * kPartialStride;
+        float *pw = part + ((long)split * BH + bh) * kPartialStride;
 #pragma unroll
-        for (int d = 0; d < 16; ++d) pw[qd * 16 + d] = acc[d];
+        for (int d = 0; d < 16; ++d) store_partial(pw + qd * 16 + d, acc[d]);
         if (qd == 0) {
-          pw[64] = m;
-          pw[65] = l;
+          store_partial(pw + 64, m);
+          store_partial(pw + 65, l);
         }
       }
     }
+    if (n_split > 1) merge_if_last(cnt, part, BH, bh, n_split, lane, vs_g, o + (long)b * os.b + (long)h * os.h);
     return;
   }
   if (r == 0) {
@@ -275,39 +354,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const float out = den > 0.f ? num / den * vs_g : 0.f;
     o[(long)b * os.b + (long)h * os.h + lane] = f32_to_bf16(out);
   } else {
-    float *pw = ws + ((long)split * (gridDim.x / n_split) + bh) * kPartialStride;
-    pw[lane] = num;
+    float *pw = part + ((long)split * BH + bh) * kPartialStride;
+    store_partial(pw + lane, num);
     if (lane == 0) {
-      pw[64] = M;
-      pw[65] = den;
+      store_partial(pw + 64, M);
+      store_partial(pw + 65, den);
     }
+    merge_if_last(cnt, part, BH, bh, n_split, lane, vs_g, o + (long)b * os.b + (long)h * os.h);
   }
-}
-
-// Combine the chunk partials of one (b, h): with M the largest chunk max,
-// o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, times the value scale.
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restrict__ ws, int BH,
-                                                          int H, int n_split,
-                                                          const float *__restrict__ vsc,
-                                                          int per_head, uint16_t *__restrict__ o,
-                                                          wa_strides os) {
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H;
-  const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int i = 0; i < n_split; ++i) M = fmaxf(M, ws[((long)i * BH + bh) * kPartialStride + 64]);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int i = 0; i < n_split; ++i) {
-      const float *pw = ws + ((long)i * BH + bh) * kPartialStride;
-      const float mi = pw[64];
-      const float e = mi == -INFINITY ? 0.f : exp2f(mi - M);
-      num = fmaf(e, pw[lane], num);
-      den = fmaf(e, pw[65], den);
-    }
-  }
-  const float out = den > 0.f ? num / den * vsc[per_head ? h : 0] : 0.f;
-  o[(long)b * os.b + (long)h * os.h + lane] = f32_to_bf16(out);
 }
 
 }  // namespace
@@ -320,7 +374,8 @@ DecodePlan decode_plan(int B, int H, int cache_len) {
   const long bh = (long)B * H;
   const int key_blocks = (cache_len + kBlockKeys - 1) / kBlockKeys;
   DecodePlan p;
-  if (bh * 4 >= kWaveSlots / 2) {
+  static_assert(kSplitPairs * 4 == kWaveSlots / 2, "the split threshold is the counters' count");
+  if (bh >= kSplitPairs) {
     p.n_split = 1;
     p.chunk = key_blocks * kBlockKeys;
     p.waves = (int)std::max<long>(1, std::min<long>(std::min(kMaxWaves, key_blocks), kWaveSlots / bh));
@@ -342,7 +397,7 @@ DecodePlan decode_plan(int B, int H, int cache_len) {
 
 size_t decode_workspace_bytes(int B, int H, const DecodePlan &p) {
   if (p.n_split <= 1) return 0;
-  return (size_t)p.n_split * B * H * kPartialStride * sizeof(float);
+  return (size_t)kCounterWords * 4 + (size_t)p.n_split * B * H * kPartialStride * sizeof(float);
 }
 
 hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, const uint8_t *vc,
@@ -360,10 +415,6 @@ hipError_t launch_decode(const uint16_t *q, wa_strides qs, const uint8_t *kc, co
     hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(BH * plan.n_split), dim3(plan.waves * 64), 0,
                        stream, q, qs, kc, vc, cs, cache_len, k_scale, v_scale, per_head, lens, H,
                        softmax_scale * kLog2e, plan.chunk, plan.n_split, ws, o, os, k_new, v_new, ns);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.n_split == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(BH), dim3(64), 0, stream, ws, BH, H, plan.n_split,
-                     v_scale, per_head, o, os);
   return hipGetLastError();
 }
 

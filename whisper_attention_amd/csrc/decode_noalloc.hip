@@ -11,20 +11,24 @@
 // copy (hipGetSymbolAddress) and keeps it; every later call uses that
 // address.
 //
-// Every call on a GPU shares its array and finds the last call's partials
-// there.  Nothing in it must start at zero: the merge reads only the slots
-// the partial kernel of the same call wrote first.  Two calls in flight at
-// once on one GPU (two streams, two host threads) race on the array.
+// Every call on a GPU shares its array and finds the last call's contents
+// there.  The array begins with the split-key calls' per-(b, h) counters,
+// which must start at zero: a device array is zero when the code object is
+// loaded, and every call leaves its counters zero again.  The partials after
+// them need no initialisation (the merge reads only what blocks of the same
+// call wrote).  Two calls in flight at once on one GPU (two streams, two host
+// threads) race on the array.
 #include <mutex>
 
 #include "wa_internal.h"
 
 namespace {
 
-// The largest partials a call can need: the planner splits the keys only
+// The largest scratch a call can need: the planner splits the keys only
 // for fewer than 640 (b, h) pairs, into at most ceil(1024 / (B*H)) chunks,
 // so n_split * B * H < 1024 + 640 and the partials stay below 1664 * 272 B
-// (452 KB).  The check below stays, in case the planner changes.
+// (452 KB), after at most 2.5 KB of counters.  The check below stays, in
+// case the planner changes.
 constexpr size_t kScratchBytes = WA_DECODE_NOALLOC_SCRATCH_BYTES;
 
 __device__ __align__(256) uint8_t scratch[kScratchBytes];
