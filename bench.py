@@ -54,7 +54,7 @@ N_SETS = 3                    # decode cache sets used in turn
 TRAFFIC = {
     "encoder_attn.hip": ("e8c76f65a8ae475b", {"encoder": 247.29e6, "prefill": 148.40e6,
                                               "fp8qk_30s": 185.51e6, "prefill_cross": 1055.60e6}),
-    "decode_attn.hip": ("c6eb9e4527d97166", {"cross": 246.21e6, "self": 42.13e6}),
+    "decode_attn.hip": ("0f745ce1c105d9f3", {"cross": 246.24e6, "self": 42.15e6}),
     "kv_dequant.hip": ("3ee61d3727638963", {"cross": 368.68e6}),
     "kv_quant.hip": ("2a006624b94a25a2", {"pair": 185.95e6}),
 }
