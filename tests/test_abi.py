@@ -51,6 +51,9 @@ def test_workspace_sizes(wa):
     assert wa.wa_kv_quant_fp8_workspace_size(3, 20, "tensor") == 768   # 256 + 3 * 32 * 4, rounded up to 256
     assert wa.lib.wa_kv_quant_fp8_workspace_size(3, 20, 7) == 0          # no such granularity
     assert wa.wa_decode_attn_workspace_size(1, 6, 1500) > 0      # split keys -> partials
+    # 640 split counters (2560 bytes), then n_split * B * H partials of 68 floats
+    n = wa.wa_decode_attn_workspace_size(1, 6, 1500)
+    assert (n - 2560) % (6 * 68 * 4) == 0 and (n - 2560) // (6 * 68 * 4) > 1
     assert wa.wa_decode_attn_workspace_size(0, 6, 1500) == 0
     # a big batch needs no split, hence no workspace
     assert wa.wa_decode_attn_workspace_size(256, 20, 1500) == 0
