@@ -21,8 +21,9 @@
 //     the query once, so a score is 16 FMAs plus a 4-lane DPP sum.
 //   * online softmax per wave in the exp2 domain, with cross-lane maxima and
 //     sums on DPP row rotations and the permlane16/32 swaps (no LDS round
-//     trips); the W waves merge in LDS; chunks of one (b, h) merge in a
-//     second small kernel (only when a (b, h) has several chunks).
+//     trips); the W waves merge in LDS; the chunks of one (b, h), when there
+//     are several, are merged by whichever chunk block finishes last (a
+//     ticket on a per-(b, h) counter), in the same launch.
 #include <algorithm>
 #include <cmath>
 
